@@ -1,0 +1,295 @@
+/*
+ * gdn_oracle.c -- plain sequential CPU oracle for the Gated DeltaNet
+ * verify / commit / rewind / conv-step / prefill path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path
+ * (libgdn.so and its Python binding) never calls it and shares no code,
+ * header, table or helper with it.
+ *
+ * Everything is computed in IEEE double with plain scalar loops, one token
+ * at a time, in the order the method states.  Inputs arrive as doubles that
+ * hold the exact values of the caller's bf16/fp32 tensors.
+ *
+ * Sources (page title, then section):
+ *  - "perf(qwen): full-context MTP draft prefill and replay-free rewind"
+ *    (Whallm PR #14), Summary item 4: linear-attention layers rerun only the
+ *    Gated DeltaNet mixer on their captured verification inputs, starting
+ *    from the pre-verification state; Tests: rewound caches are compared
+ *    with a direct forward over the accepted prefix.
+ *  - "MTP inference: review and commit structure" (eole docs), Functional
+ *    commits items 2 and 4: accepted-prefix state replay, short convolution
+ *    with a mutated convolution cache; Verification and limits: partial
+ *    commits replay only the accepted recurrent prefix, and a chunked
+ *    recurrence only rounds differently from the sequential one.
+ *  - "Add request-owned eight-way MTP serving for Qwen 35B" (MTPLX PR #245),
+ *    What was broken items 2 and 4: commit keep in {0,1,2}, keep=0 restores
+ *    the snapshotted pre-verification recurrent state, inactive rows keep
+ *    their state; item 6: rows are separable.
+ *  - The recurrence itself, S_t = a_t S_{t-1} (I - b_t k_t k_t^T)
+ *    + b_t v_t k_t^T with the output read from S_t and q_t, is the gated
+ *    delta rule (Yang, Kautz, Hatamizadeh, "Gated Delta Networks", ICLR
+ *    2025); the pages name the mixer but never print it.
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *  - storage h = S^T, h[i][j] with i over d_k and j over d_v (j contiguous);
+ *    p = h^T k, u = beta (v - a p), h <- a h + k u^T, o = scale h^T q,
+ *    with o taken from the updated state.
+ *  - conv window W = [conv_state[0..K-2] (oldest first) ; x[0..T-1]],
+ *    y_t[c] = sum_j w[c][j] W[t+j][c] (+ bias), then SiLU.
+ *  - channels ordered [q heads | k heads | v heads]; value head h reads qk
+ *    head h / (HV/HK).
+ *  - q and k are divided by sqrt(sum of squares + eps) per qk head.
+ *  - the gate is passed as g = log a (so a = exp g).
+ *  - commit(keep): keep tokens of the window enter the committed state;
+ *    keep = 0 (or an inactive row) writes nothing.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORA_FLAG_CONV_SILU 1u
+#define ORA_FLAG_QK_L2NORM 2u
+
+typedef struct {
+    int32_t L, B, T, HV, HK, DK, DV, KCONV, S;
+    double scale, l2_eps;
+    uint32_t flags;
+} ora_dims;
+
+static int nchan(const ora_dims* d) { return 2 * d->HK * d->DK + d->HV * d->DV; }
+
+/* Window row r (0 <= r < KCONV-1+T) of the conv input for one (l, b):
+ * rows 0..KCONV-2 come from conv_state, the rest from x. */
+static const double* window_row(const ora_dims* d, const double* cs_lb, const double* x_lb, int r)
+{
+    int C = nchan(d);
+    int km1 = d->KCONV - 1;
+    if (r < km1) return cs_lb + (size_t)r * C;
+    return x_lb + (size_t)(r - km1) * C;
+}
+
+/* Causal depthwise conv + optional SiLU for window token t -> y[C]. */
+static void conv_token(const ora_dims* d, const double* cs_lb, const double* x_lb,
+                       const double* w_l, const double* b_l, int t, double* y)
+{
+    int C = nchan(d);
+    for (int c = 0; c < C; ++c) {
+        double acc = 0.0;
+        for (int j = 0; j < d->KCONV; ++j)
+            acc += w_l[(size_t)c * d->KCONV + j] * window_row(d, cs_lb, x_lb, t + j)[c];
+        if (b_l) acc += b_l[c];
+        if (d->flags & ORA_FLAG_CONV_SILU) acc = acc / (1.0 + exp(-acc));
+        y[c] = acc;
+    }
+}
+
+/* One token of the gated delta rule for every value head of one (l, b).
+ * y: post-conv channels [q | k | v]; h: [HV][DK][DV] updated in place;
+ * o: [HV][DV] or NULL. */
+static void delta_token(const ora_dims* d, const double* y, const double* g_t,
+                        const double* beta_t, double* h, double* o)
+{
+    int DK = d->DK, DV = d->DV;
+    int group = d->HV / d->HK;
+    double* q = (double*)malloc(sizeof(double) * DK);
+    double* k = (double*)malloc(sizeof(double) * DK);
+    for (int hv = 0; hv < d->HV; ++hv) {
+        int m = hv / group;
+        const double* qsrc = y + (size_t)m * DK;
+        const double* ksrc = y + (size_t)d->HK * DK + (size_t)m * DK;
+        const double* v = y + (size_t)2 * d->HK * DK + (size_t)hv * DV;
+        for (int i = 0; i < DK; ++i) { q[i] = qsrc[i]; k[i] = ksrc[i]; }
+        if (d->flags & ORA_FLAG_QK_L2NORM) {
+            double sq = 0.0, sk = 0.0;
+            for (int i = 0; i < DK; ++i) { sq += q[i] * q[i]; sk += k[i] * k[i]; }
+            double nq = sqrt(sq + d->l2_eps), nk = sqrt(sk + d->l2_eps);
+            for (int i = 0; i < DK; ++i) { q[i] /= nq; k[i] /= nk; }
+        }
+        double a = exp(g_t[hv]);
+        double beta = beta_t[hv];
+        double* hh = h + (size_t)hv * DK * DV;
+        for (int j = 0; j < DV; ++j) {
+            double p = 0.0;
+            for (int i = 0; i < DK; ++i) p += hh[(size_t)i * DV + j] * k[i];
+            double u = beta * (v[j] - a * p);
+            for (int i = 0; i < DK; ++i)
+                hh[(size_t)i * DV + j] = a * hh[(size_t)i * DV + j] + k[i] * u;
+            if (o) {
+                double r = 0.0;
+                for (int i = 0; i < DK; ++i) r += hh[(size_t)i * DV + j] * q[i];
+                o[(size_t)hv * DV + j] = d->scale * r;
+            }
+        }
+    }
+    free(q);
+    free(k);
+}
+
+static size_t tile_elems(const ora_dims* d) { return (size_t)d->HV * d->DK * d->DV; }
+
+static double* slot_ptr(const ora_dims* d, double* state, int l, int b, int s)
+{
+    return state + (((size_t)l * d->B + b) * d->S + s) * tile_elems(d);
+}
+
+static int row_active(const uint8_t* active, int b) { return active ? active[b] != 0 : 1; }
+
+/* Standalone conv step: y for every token of every active row; if
+ * commit_state, the conv cache becomes the last KCONV-1 window rows. */
+void ora_conv_step(const ora_dims* d, const double* x, const double* conv_w, const double* conv_b,
+                   double* conv_state, double* y, const uint8_t* active, int commit_state)
+{
+    int C = nchan(d), km1 = d->KCONV - 1;
+    for (int l = 0; l < d->L; ++l)
+        for (int b = 0; b < d->B; ++b) {
+            if (!row_active(active, b)) continue;
+            double* cs = conv_state + ((size_t)l * d->B + b) * km1 * C;
+            const double* xl = x + ((size_t)l * d->B + b) * d->T * C;
+            const double* w = conv_w + (size_t)l * C * d->KCONV;
+            const double* bias = conv_b ? conv_b + (size_t)l * C : NULL;
+            for (int t = 0; t < d->T; ++t)
+                conv_token(d, cs, xl, w, bias, t, y + (((size_t)l * d->B + b) * d->T + t) * C);
+            if (commit_state) {
+                double* nw = (double*)malloc(sizeof(double) * km1 * C);
+                for (int r = 0; r < km1; ++r)
+                    memcpy(nw + (size_t)r * C, window_row(d, cs, xl, d->T + r), sizeof(double) * C);
+                memcpy(cs, nw, sizeof(double) * km1 * C);
+                free(nw);
+            }
+        }
+}
+
+/* Verify: from slot cur, run the T window tokens; token t's state is the
+ * candidate stored in slot (cur + t + 1) mod S, its output goes to o[t].
+ * Inactive rows write nothing.  Returns error bits (bit 1: cur out of range). */
+int ora_verify(const ora_dims* d, const double* x, const double* conv_w, const double* conv_b,
+               const double* conv_state, const double* g, const double* beta, double* state,
+               const int32_t* cur, double* o, const uint8_t* active)
+{
+    int C = nchan(d), km1 = d->KCONV - 1, err = 0;
+    size_t te = tile_elems(d);
+    double* h = (double*)malloc(sizeof(double) * te);
+    double* y = (double*)malloc(sizeof(double) * C);
+    for (int l = 0; l < d->L; ++l)
+        for (int b = 0; b < d->B; ++b) {
+            if (!row_active(active, b)) continue;
+            int c0 = cur ? cur[l * d->B + b] : 0;
+            if (c0 < 0 || c0 >= d->S) { err |= 2; continue; }
+            memcpy(h, slot_ptr(d, state, l, b, c0), sizeof(double) * te);
+            const double* cs = conv_state + ((size_t)l * d->B + b) * km1 * C;
+            const double* xl = x + ((size_t)l * d->B + b) * d->T * C;
+            const double* w = conv_w + (size_t)l * C * d->KCONV;
+            const double* bias = conv_b ? conv_b + (size_t)l * C : NULL;
+            for (int t = 0; t < d->T; ++t) {
+                size_t lbt = ((size_t)l * d->B + b) * d->T + t;
+                conv_token(d, cs, xl, w, bias, t, y);
+                delta_token(d, y, g + lbt * d->HV, beta + lbt * d->HV, h,
+                            o + lbt * d->HV * d->DV);
+                memcpy(slot_ptr(d, state, l, b, (c0 + t + 1) % d->S), h, sizeof(double) * te);
+            }
+        }
+    free(h);
+    free(y);
+    return err;
+}
+
+/* Row error bits shared by commit and rewind. */
+static int row_errors(const ora_dims* d, int keep, int c0, int act)
+{
+    int e = 0;
+    if (keep < 0 || keep > d->T) e |= 1;
+    if (c0 < 0 || c0 >= d->S) e |= 2;
+    if (!act && keep != 0) e |= 4;
+    return e;
+}
+
+/* Commit: for active rows with keep >= 1 advance the slot index by keep and
+ * make the conv cache the KCONV-1 window rows that follow the kept tokens.
+ * keep = 0 or an inactive row leaves everything untouched. */
+int ora_commit(const ora_dims* d, const double* x, double* conv_state, int32_t* cur,
+               const int32_t* keep, const uint8_t* active)
+{
+    int C = nchan(d), km1 = d->KCONV - 1, err = 0;
+    for (int l = 0; l < d->L; ++l)
+        for (int b = 0; b < d->B; ++b) {
+            int kp = keep[b];
+            int c0 = cur[l * d->B + b];
+            int act = row_active(active, b);
+            int e = row_errors(d, kp, c0, act);
+            if (e) { err |= e; continue; }
+            if (!act || kp == 0) continue;
+            cur[l * d->B + b] = (c0 + kp) % d->S;
+            double* cs = conv_state + ((size_t)l * d->B + b) * km1 * C;
+            const double* xl = x + ((size_t)l * d->B + b) * d->T * C;
+            double* nw = (double*)malloc(sizeof(double) * km1 * C);
+            for (int r = 0; r < km1; ++r)
+                memcpy(nw + (size_t)r * C, window_row(d, cs, xl, kp + r), sizeof(double) * C);
+            memcpy(cs, nw, sizeof(double) * km1 * C);
+            free(nw);
+        }
+    return err;
+}
+
+/* Rewind: replay the first keep[b] captured window tokens from the snapshot
+ * in slot cur, write the result back into slot cur and commit the conv
+ * cache as commit does.  keep = 0 touches nothing. */
+int ora_rewind(const ora_dims* d, const double* x, const double* conv_w, const double* conv_b,
+               double* conv_state, const double* g, const double* beta, double* state,
+               const int32_t* cur, const int32_t* keep, double* o)
+{
+    int C = nchan(d), km1 = d->KCONV - 1, err = 0;
+    size_t te = tile_elems(d);
+    double* h = (double*)malloc(sizeof(double) * te);
+    double* y = (double*)malloc(sizeof(double) * C);
+    for (int l = 0; l < d->L; ++l)
+        for (int b = 0; b < d->B; ++b) {
+            int kp = keep[b];
+            int c0 = cur ? cur[l * d->B + b] : 0;
+            int e = row_errors(d, kp, c0, 1);
+            if (e) { err |= e; continue; }
+            if (kp == 0) continue;
+            double* slot = slot_ptr(d, state, l, b, c0);
+            memcpy(h, slot, sizeof(double) * te);
+            double* cs = conv_state + ((size_t)l * d->B + b) * km1 * C;
+            const double* xl = x + ((size_t)l * d->B + b) * d->T * C;
+            const double* w = conv_w + (size_t)l * C * d->KCONV;
+            const double* bias = conv_b ? conv_b + (size_t)l * C : NULL;
+            for (int t = 0; t < kp; ++t) {
+                size_t lbt = ((size_t)l * d->B + b) * d->T + t;
+                conv_token(d, cs, xl, w, bias, t, y);
+                delta_token(d, y, g + lbt * d->HV, beta + lbt * d->HV, h,
+                            o ? o + lbt * d->HV * d->DV : NULL);
+            }
+            memcpy(slot, h, sizeof(double) * te);
+            double* nw = (double*)malloc(sizeof(double) * km1 * C);
+            for (int r = 0; r < km1; ++r)
+                memcpy(nw + (size_t)r * C, window_row(d, cs, xl, kp + r), sizeof(double) * C);
+            memcpy(cs, nw, sizeof(double) * km1 * C);
+            free(nw);
+        }
+    free(h);
+    free(y);
+    return err;
+}
+
+/* Prefill: the same recurrence over every token of y (post-conv channels),
+ * one token at a time, updating slot cur in place. */
+int ora_prefill(const ora_dims* d, const double* y, const double* g, const double* beta,
+                double* state, const int32_t* cur, double* o)
+{
+    int C = nchan(d), err = 0;
+    for (int l = 0; l < d->L; ++l)
+        for (int b = 0; b < d->B; ++b) {
+            int c0 = cur ? cur[l * d->B + b] : 0;
+            if (c0 < 0 || c0 >= d->S) { err |= 2; continue; }
+            double* h = slot_ptr(d, state, l, b, c0);
+            for (int t = 0; t < d->T; ++t) {
+                size_t lbt = ((size_t)l * d->B + b) * d->T + t;
+                delta_token(d, y + lbt * C, g + lbt * d->HV, beta + lbt * d->HV, h,
+                            o + lbt * d->HV * d->DV);
+            }
+        }
+    return err;
+}
