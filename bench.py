@@ -1,0 +1,404 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet verify + commit cycle on one MI355X.
+
+Headline: the B8/T2 verification cohort (32 value heads, 16 qk heads,
+d_k = d_v = 128, bf16 inputs, fp32 state, rows 1 and 6 inactive, keep ~
+U{0,1,2} drawn per cycle).  One step is one decode cycle of a 30-layer
+hybrid stack: gdn_verify over the 30 GDN layers' state pools (one grouped
+launch) followed by gdn_commit of every layer (one grouped launch).  The 30
+pools (1.44 GiB of fp32 state) exceed the 256 MiB Infinity Cache, so state
+traffic is HBM traffic.  Metric: rows*heads/s = 30 * 8 * 32 per step / time.
+
+Also printed (in the same JSON line, under "extra"): the same cycle with one
+verify launch per layer captured in a HIP graph, the solo B1/T3 30-layer
+cycle, the B8/T4 rewind, the 1,024-token conv step and the chunked prefill.
+
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+L_POOL = 30
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-headline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on torch's current stream, which is the stream every
+    libgdn call below is launched on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def ev(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+
+def cohort_pools(torch, W, sh, L, seed):
+    """L layers of the cohort: every tensor on the GPU, stacked along the layer axis."""
+    big = sh.with_(L=L)
+    rng = np.random.default_rng(seed)
+    bf = torch.bfloat16 if sh.act == "bf16" else torch.float32
+    C = sh.C
+
+    def act(shape, scale=1.0):
+        return (scale * torch.randn(shape, generator=gen, device="cuda")).to(bf)
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    t = {}
+    t["x"] = act((L, sh.B, sh.T, C))
+    t["conv_w"] = act((L, C, 4), 0.5)
+    t["conv_state"] = act((L, sh.B, 3, C))
+    t["g"] = (-torch.nn.functional.softplus(torch.randn((L, sh.B, sh.T, sh.HV), generator=gen,
+                                                        device="cuda"))).to(bf)
+    t["beta"] = torch.sigmoid(torch.randn((L, sh.B, sh.T, sh.HV), generator=gen,
+                                          device="cuda")).to(bf)
+    t["state"] = 0.1 * torch.randn((L, sh.B, sh.S, sh.HV, sh.DK, sh.DV), generator=gen,
+                                   device="cuda")
+    t["cur"] = torch.zeros((L, sh.B), dtype=torch.int32, device="cuda")
+    act_rows = np.ones(sh.B, np.uint8)
+    for r in sh.inactive:
+        act_rows[r] = 0
+    t["active"] = torch.from_numpy(act_rows).cuda()
+    t["o"] = torch.empty((L, sh.B, sh.T, sh.HV, sh.DV), dtype=torch.float32, device="cuda")
+    t["err"] = torch.zeros(1, dtype=torch.int32, device="cuda")
+    return big, t, rng, act_rows
+
+
+def verify_bytes(sh, n_active_rows, L):
+    """Algorithmic bytes of one grouped verify launch: per active (layer, row):
+    the fp32 state read once (HV*DK*DV*4) and written T times as candidates,
+    the window inputs x (T*C) and conv cache (3*C) in the act dtype, g and
+    beta (2*T*HV), and the fp32 outputs (T*HV*DV*4); per layer the conv
+    weights (C*4)."""
+    esz = 2 if sh.act == "bf16" else 4
+    tile = sh.HV * sh.DK * sh.DV * 4
+    per_row = tile * (1 + sh.T) + (sh.T + 3) * sh.C * esz + 2 * sh.T * sh.HV * esz \
+        + sh.T * sh.HV * sh.DV * 4
+    return L * (n_active_rows * per_row + sh.C * 4 * esz)
+
+
+def commit_bytes(sh, keep, active, L):
+    """Per committing (layer, row): 3 conv-cache rows written and the 3
+    window rows they come from read (act dtype), plus keep/active/cur."""
+    esz = 2 if sh.act == "bf16" else 4
+    n = int(np.sum((keep > 0) & (active > 0)))
+    return L * (n * 6 * sh.C * esz + sh.B * 9)
+
+
+def headline(torch, gb, W, args):
+    sh = W.COHORT
+    big, t, rng, act_rows = cohort_pools(torch, W, sh, L_POOL, 1001)
+    d = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
+                     out="f32")
+    n = args.steps + args.warmup
+    keeps = np.stack([W.keep_uniform(rng, sh, act_rows) for _ in range(n)]).astype(np.int32)
+    keep_d = torch.from_numpy(keeps).cuda()
+
+    def step(i):
+        gb.gdn_verify(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
+                      t["state"], t["cur"], t["o"], t["active"], t["err"])
+        gb.gdn_commit(d, t["x"], t["conv_state"], t["cur"], keep_d[i], t["active"], t["err"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    marks = []
+    start = tm.ev()
+    for i in range(args.warmup, n):
+        v0 = tm.ev()
+        gb.gdn_verify(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
+                      t["state"], t["cur"], t["o"], t["active"], t["err"])
+        v1 = tm.ev()
+        gb.gdn_commit(d, t["x"], t["conv_state"], t["cur"], keep_d[i], t["active"], t["err"])
+        marks.append((v0, v1))
+    end = tm.ev()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    verify_ms = float(np.mean([a.elapsed_time(b) for a, b in marks]))
+    assert int(t["err"].item()) == 0, "device error word set"
+    n_act = int(act_rows.sum())
+    vb = verify_bytes(sh, n_act, L_POOL)
+    cb = float(np.mean([commit_bytes(sh, keeps[i], act_rows, L_POOL) for i in range(args.warmup, n)]))
+    ms_step = total_ms / args.steps
+    rows_heads = L_POOL * sh.B * sh.HV
+    res = dict(ms_per_step=ms_step, value=rows_heads * args.steps / (total_ms / 1e3),
+               verify_ms=verify_ms, verify_bytes=vb, commit_bytes=cb,
+               verify_gbs=vb / (verify_ms / 1e3) / 1e9,
+               cycle_gbs=(vb + cb) / (ms_step / 1e3) / 1e9,
+               active_rows_heads_per_s=L_POOL * n_act * sh.HV * args.steps / (total_ms / 1e3))
+    del t
+    torch.cuda.empty_cache()
+    return res
+
+
+def per_layer_graph(torch, gb, W, args):
+    """The same cycle with one verify launch per layer (as a model forward
+    issues them), captured once in a HIP graph and replayed."""
+    sh = W.COHORT
+    big, t, rng, act_rows = cohort_pools(torch, W, sh, L_POOL, 1002)
+    d1 = gb.make_dims(1, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16", out="f32")
+    dL = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
+                      out="f32")
+    keep_cur = torch.zeros(sh.B, dtype=torch.int32, device="cuda")
+    n = args.steps + args.warmup
+    keeps = torch.from_numpy(np.stack([W.keep_uniform(rng, sh, act_rows) for _ in range(n)])
+                             .astype(np.int32)).cuda()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+
+    def cycle():
+        for l in range(L_POOL):
+            sl = slice(l, l + 1)
+            gb.gdn_verify(d1, t["x"][sl], t["conv_w"][sl], None, t["conv_state"][sl],
+                          t["g"][sl], t["beta"][sl], t["state"][sl], t["cur"][sl], t["o"][sl],
+                          t["active"], t["err"])
+        gb.gdn_commit(dL, t["x"], t["conv_state"], t["cur"], keep_cur, t["active"], t["err"])
+
+    with torch.cuda.stream(s):
+        cycle()                       # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        cycle()
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        keep_cur.copy_(keeps[i])
+        graph.replay()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    start = tm.ev()
+    for i in range(args.warmup, n):
+        keep_cur.copy_(keeps[i])
+        graph.replay()
+    end = tm.ev()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    assert int(t["err"].item()) == 0
+    res = dict(ms_per_step=ms, rows_heads_per_s=L_POOL * sh.B * sh.HV / (ms / 1e3),
+               launches_per_step=L_POOL + 1)
+    del graph, t
+    torch.cuda.empty_cache()
+    return res
+
+
+def solo(torch, gb, W, args):
+    """B=1, T=3 (two drafts + bonus), 30 independent layers in one grouped
+    launch, keep by prefix acceptance p=0.8, state carried across cycles."""
+    sh = W.SOLO
+    big, t, rng, act_rows = cohort_pools(torch, W, sh.with_(L=1), sh.L, 2002)
+    d = gb.make_dims(sh.L, 1, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16", out="f32")
+    cycles = 200
+    keeps = torch.from_numpy(np.stack([W.keep_prefix_acceptance(rng, sh) for _ in range(cycles)])
+                             .astype(np.int32)).cuda()
+
+    def cyc(i):
+        gb.gdn_verify(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
+                      t["state"], t["cur"], t["o"], None, t["err"])
+        gb.gdn_commit(d, t["x"], t["conv_state"], t["cur"], keeps[i], None, t["err"])
+
+    for i in range(10):
+        cyc(i)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    marks = []
+    start = tm.ev()
+    for i in range(cycles):
+        v0 = tm.ev()
+        gb.gdn_verify(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
+                      t["state"], t["cur"], t["o"], None, t["err"])
+        v1 = tm.ev()
+        gb.gdn_commit(d, t["x"], t["conv_state"], t["cur"], keeps[i], None, t["err"])
+        marks.append((v0, v1))
+    end = tm.ev()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / cycles
+    vms = float(np.mean([a.elapsed_time(b) for a, b in marks]))
+    vb = verify_bytes(sh, 1, sh.L)
+    assert int(t["err"].item()) == 0
+    del t
+    torch.cuda.empty_cache()
+    return dict(ms_per_cycle=ms, rows_heads_per_s=sh.L * sh.HV / (ms / 1e3), verify_ms=vms,
+                verify_gbs=vb / (vms / 1e3) / 1e9)
+
+
+def rewind(torch, gb, W, args):
+    """B=8, T=4 captured window, keep ~ U{0..4}, 30 layer pools in one grouped call."""
+    sh = W.REWIND
+    big, t, rng, act_rows = cohort_pools(torch, W, sh.with_(L=1), L_POOL, 3003)
+    d = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
+                     out="f32")
+    reps = 20
+    keeps_np = np.stack([W.keep_uniform(rng, sh) for _ in range(reps + 3)]).astype(np.int32)
+    keeps = torch.from_numpy(keeps_np).cuda()
+    for i in range(3):
+        gb.gdn_rewind(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
+                      t["state"], t["cur"], keeps[i], None, t["err"])
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    start = tm.ev()
+    for i in range(3, reps + 3):
+        gb.gdn_rewind(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
+                      t["state"], t["cur"], keeps[i], None, t["err"])
+    end = tm.ev()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    tile = sh.HV * sh.DK * sh.DV * 4
+    k = keeps_np[3:]
+    # per committing (layer, row): state read + written, keep tokens of x/g/beta,
+    # conv cache read + written (3 rows each)
+    per_call = np.mean([L_POOL * sum(2 * tile + kk * (sh.C * 2 + 4 * sh.HV) + 9 * sh.C * 2
+                                     for kk in row if kk > 0) for row in k])
+    assert int(t["err"].item()) == 0
+    del t
+    torch.cuda.empty_cache()
+    return dict(ms_per_call=ms, bytes_per_call=float(per_call),
+                gbs=per_call / (ms / 1e3) / 1e9,
+                rows_heads_per_s=L_POOL * sh.B * sh.HV / (ms / 1e3))
+
+
+def conv_step(torch, gb, W, args):
+    """The standalone conv over a 1,024-token prefill call, 10 buffers rotated."""
+    sh = W.PREFILL
+    nb = 10
+    C = sh.C
+    bf = torch.bfloat16
+    xs = [torch.randn((1, 1, sh.T, C), device="cuda").to(bf) for _ in range(nb)]
+    ys = [torch.empty((1, 1, sh.T, C), device="cuda", dtype=bf) for _ in range(nb)]
+    w = (0.5 * torch.randn((1, C, 4), device="cuda")).to(bf)
+    cs = torch.randn((1, 1, 3, C), device="cuda").to(bf)
+    d = gb.make_dims(1, 1, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=1, act="bf16", out="bf16")
+    for i in range(nb):
+        gb.gdn_conv_step(d, xs[i], w, None, cs, ys[i], None, True)
+    torch.cuda.synchronize()
+    reps = 50
+    tm = Timer(torch)
+    start = tm.ev()
+    for i in range(reps):
+        gb.gdn_conv_step(d, xs[i % nb], w, None, cs, ys[i % nb], None, True)
+    end = tm.ev()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    byts = 2 * sh.T * C * 2 + C * 4 * 2 + 6 * C * 2
+    return dict(tokens=sh.T, ms_per_call=ms, gbs=byts / (ms / 1e3) / 1e9)
+
+
+def cpu_baseline(W, budget_s=12.0):
+    """The oracle as it stands (single-threaded C, float64) on a bounded
+    sample of the headline workload: whole verify + commit layer-cycles of
+    the B8/T2 cohort (8 rows x 32 heads each) until the time budget is used."""
+    import oracle
+    sh = W.COHORT
+    inp = W.verify_inputs(sh, seed=4242)
+    od = oracle.Dims(L=1, B=sh.B, T=sh.T, HV=sh.HV, HK=sh.HK, DK=sh.DK, DV=sh.DV, S=sh.S)
+    rng = np.random.default_rng(1)
+    st, cs, cur = inp["state"], inp["conv_state"], inp["cur"]
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        keep = W.keep_uniform(rng, sh, inp["active"])
+        st, _, _ = oracle.verify(od, inp["x"], inp["conv_w"], None, cs, inp["g"], inp["beta"],
+                                 st, cur, inp["active"])
+        cs, cur, _ = oracle.commit(od, inp["x"], cs, cur, keep, inp["active"])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 400:
+            break
+    return dict(value=n * sh.B * sh.HV / el, unit="rows*heads/s", cores=1, kind="oracle",
+                sample="%d verify+commit layer-cycles of the B8/T2 cohort (8 rows x 32 heads, "
+                       "6 active) in %.1f s, single-threaded float64 C oracle incl. marshalling; "
+                       "host: %s, %d cpus" % (n, el, platform.processor() or platform.machine(),
+                                              os.cpu_count() or 0))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this path has no cross-GPU exchange and the "
+              "build runs on single-GPU boxes; --gpus %d is not supported" % max(args.gpus, world),
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from gated_deltanet_recurrence_conv_amd import binding as gb
+    from gated_deltanet_recurrence_conv_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log("bench: %s on %s" % (gb.gdn_version(), torch.cuda.get_device_name(0)))
+    log("bench: headline B8/T2 cohort x %d layers, %d steps" % (L_POOL, args.steps))
+    h = headline(torch, gb, W, args)
+    log("bench: headline %.4f ms/step  verify %.1f GB/s" % (h["ms_per_step"], h["verify_gbs"]))
+    extra = {}
+    if not args.only_headline:
+        for name, fn in (("per_layer_graph_b8_t2", per_layer_graph), ("solo_b1_t3_l30", solo),
+                         ("rewind_b8_t4", rewind), ("conv_step_t1024", conv_step)):
+            log("bench: %s" % name)
+            extra[name] = fn(torch, gb, W, args)
+            log("bench: %s -> %s" % (name, json.dumps(extra[name])))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (oracle)")
+        cpu = cpu_baseline(W)
+    vb = h["verify_bytes"]
+    rec = {
+        "metric": "GDN verify+commit rows*heads/s (B8,T2,32 heads) + achieved HBM GB/s vs peak",
+        "value": h["value"],
+        "unit": "rows*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": "qwen_verify_cohort_b8_t2_hv32_hk16_d128 x %d layer pools "
+                               "(grouped verify + grouped commit per cycle)" % L_POOL,
+                   "rows": 8, "active_rows": 6, "T": 2, "value_heads": 32, "qk_heads": 16,
+                   "d_k": 128, "d_v": 128, "layers": L_POOL, "inputs": "bf16",
+                   "state": "fp32", "keep": "U{0,1,2} per cycle"},
+        "roofline": {"bound": "hbm", "kernel": "gdn::recurrent_kernel<128,128,bf16> (verify)",
+                     "achieved": h["verify_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": h["verify_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": vb,
+                     "avg_launch_ms": h["verify_ms"]},
+        "cycle_gbs": h["cycle_gbs"],
+        "active_rows_heads_per_s": h["active_rows_heads_per_s"],
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,228 @@
+"""Thin Python binding of libgdn.so (the C ABI declared in include/gdn.h).
+
+Argument marshalling only: every function takes torch tensors that live on
+the GPU (or raw device addresses as ints), checks that each one has the
+dtype, size and layout the dims imply -- so that no kernel can be launched
+on a buffer smaller than its grid assumes -- and calls the C entry point of
+the same name on the current torch stream.  All arithmetic happens in the
+HIP kernels; there is no CPU path.  Importing this module fails loudly if
+libgdn.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libgdn.so is not built (expected at %s); run "
+                      "`python -m gated_deltanet_recurrence_conv_amd.build` -- there is no "
+                      "fallback path" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+GDN_OK = 0
+STATUS_NAMES = {0: "GDN_OK", 1: "GDN_E_NULL", 2: "GDN_E_SHAPE", 3: "GDN_E_DTYPE",
+                4: "GDN_E_ALIGN", 5: "GDN_E_UNSUPPORTED", 6: "GDN_E_WORKSPACE", 7: "GDN_E_HIP"}
+GDN_F32, GDN_BF16 = 0, 1
+FLAG_CONV_SILU, FLAG_QK_L2NORM = 1, 2
+ERR_KEEP, ERR_SLOT, ERR_INACTIVE_KEEP = 1, 2, 4
+
+
+class gdn_dims(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("B", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("HV", ctypes.c_int32), ("HK", ctypes.c_int32), ("DK", ctypes.c_int32),
+                ("DV", ctypes.c_int32), ("KCONV", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("out", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
+                ("flags", ctypes.c_uint32)]
+
+
+_DT = {"f32": GDN_F32, "fp32": GDN_F32, "float32": GDN_F32, "bf16": GDN_BF16,
+       "bfloat16": GDN_BF16}
+
+
+def make_dims(L, B, T, HV, HK, DK, DV, S=1, act="bf16", out="f32", scale=1.0, l2_eps=1e-6,
+              flags=FLAG_CONV_SILU | FLAG_QK_L2NORM, KCONV=4) -> gdn_dims:
+    return gdn_dims(int(L), int(B), int(T), int(HV), int(HK), int(DK), int(DV), int(KCONV),
+                    int(S), _DT[act] if isinstance(act, str) else int(act),
+                    _DT[out] if isinstance(out, str) else int(out), float(scale),
+                    float(l2_eps), int(flags))
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.gdn_status_string(status)
+        super().__init__("%s: %s" % (where, msg.decode() if msg else STATUS_NAMES.get(status)))
+
+
+_vp, _i32 = ctypes.c_void_p, ctypes.c_int32
+_D = ctypes.POINTER(gdn_dims)
+_lib.gdn_conv_step.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _vp]
+_lib.gdn_verify.argtypes = [_D] + [_vp] * 12
+_lib.gdn_commit.argtypes = [_D] + [_vp] * 7
+_lib.gdn_rewind.argtypes = [_D] + [_vp] * 12
+_lib.gdn_prefill_chunked.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                     ctypes.c_size_t, _vp, _vp]
+_lib.gdn_workspace_size.argtypes = [_D, _i32]
+_lib.gdn_workspace_size.restype = ctypes.c_size_t
+_lib.gdn_status_string.argtypes = [ctypes.c_int]
+_lib.gdn_status_string.restype = ctypes.c_char_p
+_lib.gdn_version.argtypes = []
+_lib.gdn_version.restype = ctypes.c_char_p
+for _n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_prefill_chunked"):
+    getattr(_lib, _n).restype = ctypes.c_int
+
+EXPORTED = ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_prefill_chunked",
+            "gdn_workspace_size", "gdn_status_string", "gdn_version")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _act_dtype(code):
+    torch = _torch()
+    return torch.bfloat16 if code == GDN_BF16 else torch.float32
+
+
+def _arg(t, name, shape=None, dtype=None, optional=False):
+    """Device address of a tensor (or an int address) after checking it."""
+    if t is None:
+        if optional:
+            return None
+        raise GdnError(1, "%s is required" % name)
+    if isinstance(t, int):
+        return t
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s: expected a torch.Tensor or a device address" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None:
+        n = 1
+        for s in shape:
+            n *= int(s)
+        if t.numel() != n:
+            raise ValueError("%s must hold %d elements for shape %s (got %d)"
+                             % (name, n, tuple(shape), t.numel()))
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return _torch().cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _shapes(d: gdn_dims):
+    C = 2 * d.HK * d.DK + d.HV * d.DV
+    return dict(x=(d.L, d.B, d.T, C), conv_w=(d.L, C, d.KCONV), conv_b=(d.L, C),
+                conv_state=(d.L, d.B, d.KCONV - 1, C), g=(d.L, d.B, d.T, d.HV),
+                state=(d.L, d.B, d.S, d.HV, d.DK, d.DV), cur=(d.L, d.B),
+                o=(d.L, d.B, d.T, d.HV, d.DV), rows=(d.B,), err=(1,))
+
+
+def _check(status, where):
+    if status != GDN_OK:
+        raise GdnError(status, where)
+
+
+def gdn_conv_step(d, x, conv_w, conv_b, conv_state, y, active=None, commit_state=True,
+                  err=None, stream=None):
+    torch, s = _torch(), _shapes(d)
+    A, O = _act_dtype(d.act), _act_dtype(d.out)
+    _check(_lib.gdn_conv_step(
+        ctypes.byref(d), _arg(x, "x", s["x"], A), _arg(conv_w, "conv_w", s["conv_w"], A),
+        _arg(conv_b, "conv_b", s["conv_b"], A, True), _arg(conv_state, "conv_state",
+                                                             s["conv_state"], A),
+        _arg(y, "y", s["x"], O), _arg(active, "active", s["rows"], torch.uint8, True),
+        int(bool(commit_state)), _arg(err, "err", s["err"], torch.int32, True),
+        _stream(stream)), "gdn_conv_step")
+
+
+def gdn_verify(d, x, conv_w, conv_b, conv_state, g, beta, state, cur, o, active=None, err=None,
+               stream=None):
+    torch, s = _torch(), _shapes(d)
+    A, O = _act_dtype(d.act), _act_dtype(d.out)
+    _check(_lib.gdn_verify(
+        ctypes.byref(d), _arg(x, "x", s["x"], A), _arg(conv_w, "conv_w", s["conv_w"], A),
+        _arg(conv_b, "conv_b", s["conv_b"], A, True),
+        _arg(conv_state, "conv_state", s["conv_state"], A), _arg(g, "g", s["g"], A),
+        _arg(beta, "beta", s["g"], A), _arg(state, "state", s["state"], torch.float32),
+        _arg(cur, "cur", s["cur"], torch.int32, True), _arg(o, "o", s["o"], O),
+        _arg(active, "active", s["rows"], torch.uint8, True),
+        _arg(err, "err", s["err"], torch.int32, True), _stream(stream)), "gdn_verify")
+
+
+def gdn_commit(d, x, conv_state, cur, keep, active=None, err=None, stream=None):
+    torch, s = _torch(), _shapes(d)
+    A = _act_dtype(d.act)
+    _check(_lib.gdn_commit(
+        ctypes.byref(d), _arg(x, "x", s["x"], A),
+        _arg(conv_state, "conv_state", s["conv_state"], A),
+        _arg(cur, "cur", s["cur"], torch.int32), _arg(keep, "keep", s["rows"], torch.int32),
+        _arg(active, "active", s["rows"], torch.uint8, True),
+        _arg(err, "err", s["err"], torch.int32, True), _stream(stream)), "gdn_commit")
+
+
+def gdn_rewind(d, x, conv_w, conv_b, conv_state, g, beta, state, cur, keep, o=None, err=None,
+               stream=None):
+    torch, s = _torch(), _shapes(d)
+    A, O = _act_dtype(d.act), _act_dtype(d.out)
+    _check(_lib.gdn_rewind(
+        ctypes.byref(d), _arg(x, "x", s["x"], A), _arg(conv_w, "conv_w", s["conv_w"], A),
+        _arg(conv_b, "conv_b", s["conv_b"], A, True),
+        _arg(conv_state, "conv_state", s["conv_state"], A), _arg(g, "g", s["g"], A),
+        _arg(beta, "beta", s["g"], A), _arg(state, "state", s["state"], torch.float32),
+        _arg(cur, "cur", s["cur"], torch.int32, True),
+        _arg(keep, "keep", s["rows"], torch.int32), _arg(o, "o", s["o"], O, True),
+        _arg(err, "err", s["err"], torch.int32, True), _stream(stream)), "gdn_rewind")
+
+
+def gdn_workspace_size(d, chunk=64) -> int:
+    return int(_lib.gdn_workspace_size(ctypes.byref(d), int(chunk)))
+
+
+def gdn_prefill_chunked(d, y, g, beta, state, cur, o, chunk=64, workspace=None, err=None,
+                        stream=None):
+    torch, s = _torch(), _shapes(d)
+    A, O = _act_dtype(d.act), _act_dtype(d.out)
+    need = gdn_workspace_size(d, chunk)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if isinstance(workspace, int):
+            raise TypeError("workspace must be a tensor so that its size is known")
+        ws_ptr = _arg(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        if ws_bytes < need:
+            raise ValueError("workspace holds %d bytes, %d needed" % (ws_bytes, need))
+    _check(_lib.gdn_prefill_chunked(
+        ctypes.byref(d), _arg(y, "y", s["x"], A), _arg(g, "g", s["g"], A),
+        _arg(beta, "beta", s["g"], A), _arg(state, "state", s["state"], torch.float32),
+        _arg(cur, "cur", s["cur"], torch.int32, True), _arg(o, "o", s["o"], O), int(chunk),
+        ws_ptr, ws_bytes, _arg(err, "err", s["err"], torch.int32, True), _stream(stream)),
+        "gdn_prefill_chunked")
+
+
+def gdn_status_string(status: int) -> str:
+    return _lib.gdn_status_string(int(status)).decode()
+
+
+def gdn_version() -> str:
+    return _lib.gdn_version().decode()
+
+
+def raw_library():
+    """The loaded ctypes library (for calls with raw pointers)."""
+    return _lib

@@ -1,0 +1,200 @@
+// gdn_api.hip -- the C ABI of libgdn.so: host-side validation, launch
+// geometry and status codes.  Every check runs before anything is launched
+// ("MTP inference: review and commit structure", Review fixes: grouped
+// replay checks all shapes, dtypes and devices before combining layers;
+// "Add request-owned eight-way MTP serving for Qwen 35B", Clean-install
+// verification: fail closed instead of falling back).  There is exactly one
+// code path per call and no host fallback.
+#include "gdn.h"
+#include "gdn_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+using gdn::RecParams;
+using gdn::WinParams;
+using gdn::ConvParams;
+
+bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int channels(const gdn_dims* d) { return 2 * d->HK * d->DK + d->HV * d->DV; }
+
+// Checks shared by every call.
+gdn_status check_dims(const gdn_dims* d)
+{
+    if (!d) return GDN_E_NULL;
+    if (d->act != GDN_F32 && d->act != GDN_BF16) return GDN_E_DTYPE;
+    if (d->out != GDN_F32 && d->out != GDN_BF16) return GDN_E_DTYPE;
+    if (d->L < 1 || d->B < 1 || d->T < 1 || d->HV < 1 || d->HK < 1 || d->S < 1)
+        return GDN_E_SHAPE;
+    if (d->HV % d->HK != 0) return GDN_E_SHAPE;
+    if (!head_dim_ok(d->DK) || !head_dim_ok(d->DV)) return GDN_E_SHAPE;
+    if (d->KCONV != 4) return GDN_E_SHAPE;
+    // Keep every element index of every array inside int64 and the grids
+    // inside their limits.
+    const long long C = channels(d);
+    if (static_cast<long long>(d->L) * d->B > 65535) return GDN_E_SHAPE;
+    if (static_cast<long long>(d->HV) * d->DK * d->DV * d->S * d->B * d->L > (1LL << 40))
+        return GDN_E_SHAPE;
+    if (C * d->T > (1LL << 31)) return GDN_E_SHAPE;
+    if (!(d->l2_eps >= 0.0f)) return GDN_E_SHAPE;
+    return GDN_OK;
+}
+
+gdn_status check_ptrs(std::initializer_list<const void*> req, std::initializer_list<const void*> opt)
+{
+    for (const void* p : req)
+        if (!p) return GDN_E_NULL;
+    for (const void* p : req)
+        if (!aligned(p)) return GDN_E_ALIGN;
+    for (const void* p : opt)
+        if (p && !aligned(p)) return GDN_E_ALIGN;
+    return GDN_OK;
+}
+
+gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
+
+RecParams rec_params(const gdn_dims* d)
+{
+    RecParams p{};
+    p.L = d->L; p.B = d->B; p.T = d->T; p.HV = d->HV; p.HK = d->HK; p.S = d->S;
+    p.C = channels(d);
+    p.act = d->act; p.out = d->out;
+    p.scale = d->scale; p.l2_eps = d->l2_eps; p.flags = d->flags;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gdn_status_string(gdn_status s)
+{
+    switch (s) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_E_NULL: return "GDN_E_NULL: a required pointer is NULL";
+    case GDN_E_SHAPE: return "GDN_E_SHAPE: a size is outside the supported range";
+    case GDN_E_DTYPE: return "GDN_E_DTYPE: act/out must be GDN_F32 or GDN_BF16";
+    case GDN_E_ALIGN: return "GDN_E_ALIGN: a pointer is not 16-byte aligned";
+    case GDN_E_UNSUPPORTED: return "GDN_E_UNSUPPORTED: not implemented for these arguments";
+    case GDN_E_WORKSPACE: return "GDN_E_WORKSPACE: workspace missing or too small";
+    case GDN_E_HIP: return "GDN_E_HIP: the HIP runtime reported a launch failure";
+    }
+    return "unknown gdn_status";
+}
+
+const char* gdn_version(void) { return "libgdn 0.1.0 (HIP, gfx950)"; }
+
+gdn_status gdn_conv_step(const gdn_dims* d, const void* x, const void* conv_w, const void* conv_b,
+                         void* conv_state, void* y, const uint8_t* active, int commit_state,
+                         int32_t* err, void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    st = check_ptrs({x, conv_w, conv_state, y}, {conv_b, err});
+    if (st != GDN_OK) return st;
+    (void)err;
+    ConvParams p{};
+    p.x = x; p.conv_w = conv_w; p.conv_b = conv_b; p.conv_state = conv_state; p.y = y;
+    p.active = active;
+    p.L = d->L; p.B = d->B; p.T = d->T; p.C = channels(d);
+    p.act = d->act; p.out = d->out; p.flags = d->flags;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = from_hip(gdn::launch_conv(p, s));
+    if (st != GDN_OK || !commit_state) return st;
+    WinParams w{};
+    w.x = x; w.conv_state = conv_state; w.active = active; w.err = err;
+    w.L = d->L; w.B = d->B; w.T = d->T; w.S = d->S; w.C = p.C; w.act = d->act;
+    w.mode = gdn::WIN_FULL;
+    return from_hip(gdn::launch_window(w, s));
+}
+
+gdn_status gdn_verify(const gdn_dims* d, const void* x, const void* conv_w, const void* conv_b,
+                      const void* conv_state, const void* g, const void* beta, float* state,
+                      const int32_t* cur, void* o, const uint8_t* active, int32_t* err,
+                      void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    if (d->T > 4 || d->S < d->T + 1) return GDN_E_SHAPE;
+    st = check_ptrs({x, conv_w, conv_state, g, beta, state, o}, {conv_b, cur, err});
+    if (st != GDN_OK) return st;
+    RecParams p = rec_params(d);
+    p.x = x; p.conv_w = conv_w; p.conv_b = conv_b; p.conv_state = conv_state;
+    p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.active = active;
+    p.keep = nullptr; p.err = err; p.mode = gdn::REC_VERIFY;
+    return from_hip(gdn::launch_recurrent(p, d->DK, d->DV, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_commit(const gdn_dims* d, const void* x, void* conv_state, int32_t* cur,
+                      const int32_t* keep, const uint8_t* active, int32_t* err, void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    if (d->T > 4 || d->S < d->T + 1) return GDN_E_SHAPE;
+    st = check_ptrs({x, conv_state, cur, keep}, {err});
+    if (st != GDN_OK) return st;
+    WinParams w{};
+    w.x = x; w.conv_state = conv_state; w.cur = cur; w.keep = keep; w.active = active;
+    w.err = err; w.L = d->L; w.B = d->B; w.T = d->T; w.S = d->S; w.C = channels(d);
+    w.act = d->act; w.mode = gdn::WIN_COMMIT;
+    return from_hip(gdn::launch_window(w, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_rewind(const gdn_dims* d, const void* x, const void* conv_w, const void* conv_b,
+                      void* conv_state, const void* g, const void* beta, float* state,
+                      const int32_t* cur, const int32_t* keep, void* o, int32_t* err,
+                      void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    if (d->T > 4) return GDN_E_SHAPE;
+    st = check_ptrs({x, conv_w, conv_state, g, beta, state, keep}, {conv_b, cur, o, err});
+    if (st != GDN_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    RecParams p = rec_params(d);
+    p.x = x; p.conv_w = conv_w; p.conv_b = conv_b; p.conv_state = conv_state;
+    p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.active = nullptr;
+    p.keep = keep; p.err = err; p.mode = gdn::REC_REWIND;
+    st = from_hip(gdn::launch_recurrent(p, d->DK, d->DV, s));
+    if (st != GDN_OK) return st;
+    // The conv cache is shifted by a second launch, after every wave of the
+    // replay has read the old cache.
+    WinParams w{};
+    w.x = x; w.conv_state = conv_state; w.cur = const_cast<int32_t*>(cur); w.keep = keep;
+    w.active = nullptr; w.err = err; w.L = d->L; w.B = d->B; w.T = d->T; w.S = d->S;
+    w.C = p.C; w.act = d->act; w.mode = gdn::WIN_REWIND;
+    return from_hip(gdn::launch_window(w, s));
+}
+
+size_t gdn_workspace_size(const gdn_dims* d, int32_t chunk)
+{
+    if (check_dims(d) != GDN_OK || chunk != 64) return 0;
+    return gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, chunk);
+}
+
+gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* y, const void* g, const void* beta,
+                               float* state, const int32_t* cur, void* o, int32_t chunk,
+                               void* workspace, size_t workspace_bytes, int32_t* err,
+                               void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    if (chunk != 64) return GDN_E_SHAPE;
+    st = check_ptrs({y, g, beta, state, o}, {cur, err, workspace});
+    if (st != GDN_OK) return st;
+    const size_t need = gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, chunk);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
+    gdn::PrefillParams p{};
+    p.y = y; p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.ws = workspace;
+    p.err = err;
+    p.L = d->L; p.B = d->B; p.T = d->T; p.HV = d->HV; p.HK = d->HK; p.S = d->S;
+    p.C = channels(d); p.act = d->act; p.out = d->out;
+    p.scale = d->scale; p.l2_eps = d->l2_eps; p.flags = d->flags;
+    return from_hip(gdn::launch_prefill(p, d->DK, d->DV, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,212 @@
+// gdn_conv.hip -- the short causal depthwise conv and its rolling cache.
+//
+// "MTP inference: review and commit structure" (eole docs), Functional
+// commits items 2 and 4: a compiled short convolution whose cache is mutated
+// in place; "Add request-owned eight-way MTP serving for Qwen 35B" (MTPLX
+// PR #245), What was broken items 2 and 4: a row commits keep tokens of its
+// verification window and keep=0 / inactive rows change nothing.
+//
+// Window of one (layer, row): W = [conv_state[0..2] (oldest first) ; x[0..T-1]],
+// y_t[c] = SiLU(sum_j w[c][j] * W[t+j][c] + b[c]).  Committing keep tokens
+// makes the cache W[keep .. keep+2].
+//
+// Both kernels are pure streaming work (HBM-bound, a few flops per byte):
+// each thread owns 16 contiguous bytes of channels (8 bf16 or 4 fp32), so a
+// wave moves 1 KiB per access and rows are read once.
+#include "gdn_internal.h"
+
+namespace gdn {
+
+// Loads/stores VEC contiguous activation values as fp32.
+template <int ACT>
+__device__ __forceinline__ void load_vec8(const void* base, size_t idx, float* v)
+{
+    if constexpr (ACT == ACT_BF16) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+__device__ __forceinline__ void store_vec8(void* base, size_t idx, int dt, const float* v)
+{
+    if (dt == ACT_BF16) {
+        uint4 raw;
+        raw.x = f32_to_bf16_bits(v[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+        raw.y = f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+        raw.z = f32_to_bf16_bits(v[4]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[5])) << 16);
+        raw.w = f32_to_bf16_bits(v[6]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[7])) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) = raw;
+    } else {
+        float4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+        *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = a;
+        *reinterpret_cast<float4*>(static_cast<float*>(base) + idx + 4) = b;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Conv-window shift.  grid = (ceil(C / (8*256)), L*B); each thread handles 8
+// channels of one (layer, row).  All three source rows are read into
+// registers before the cache is overwritten.
+__global__ __launch_bounds__(256) void window_kernel(WinParams p)
+{
+    const int lb = blockIdx.y;
+    const int b = lb % p.B;
+    const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+
+    int shift;
+    if (p.mode == WIN_FULL) {
+        if (p.active && p.active[b] == 0) return;
+        shift = p.T;
+    } else {
+        const int kp = p.keep[b];
+        const int slot = p.cur ? p.cur[lb] : 0;
+        const bool act = p.mode == WIN_REWIND ? true : (p.active ? p.active[b] != 0 : true);
+        int e = 0;
+        if (kp < 0 || kp > p.T) e |= ERR_KEEP;
+        if (slot < 0 || slot >= p.S) e |= ERR_SLOT;
+        if (!act && kp != 0) e |= ERR_INACTIVE_KEEP;
+        if (e) {
+            if (blockIdx.x == 0 && threadIdx.x == 0 && p.err) atomicOr(p.err, e);
+            return;
+        }
+        if (!act || kp == 0) return;
+        // Only block 0 advances the slot.  Other blocks of this row read cur
+        // solely for the range check above, which the new value also passes.
+        if (p.mode == WIN_COMMIT && blockIdx.x == 0 && threadIdx.x == 0)
+            p.cur[lb] = (slot + kp) % p.S;
+        shift = kp;
+    }
+    if (c0 >= p.C) return;
+
+    const int esz = p.act == ACT_BF16 ? 2 : 4;
+    // Stage the three new rows: W[shift + r], r = 0..2.
+    uint4 buf[3][2];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        const int q = shift + r;
+        const char* src;
+        if (q < 3)
+            src = static_cast<const char*>(p.conv_state) +
+                  ((static_cast<size_t>(lb) * 3 + q) * p.C + c0) * esz;
+        else
+            src = static_cast<const char*>(p.x) +
+                  ((static_cast<size_t>(lb) * p.T + (q - 3)) * p.C + c0) * esz;
+        buf[r][0] = reinterpret_cast<const uint4*>(src)[0];
+        if (esz == 4) buf[r][1] = reinterpret_cast<const uint4*>(src)[1];
+    }
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        char* dst = static_cast<char*>(p.conv_state) + ((static_cast<size_t>(lb) * 3 + r) * p.C + c0) * esz;
+        reinterpret_cast<uint4*>(dst)[0] = buf[r][0];
+        if (esz == 4) reinterpret_cast<uint4*>(dst)[1] = buf[r][1];
+    }
+}
+
+hipError_t launch_window(const WinParams& p, hipStream_t s)
+{
+    const int per_row = (p.C + 8 * 256 - 1) / (8 * 256);
+    const long long rows = static_cast<long long>(p.L) * p.B;
+    if (rows > 65535 || rows <= 0) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(window_kernel, dim3(per_row, static_cast<unsigned>(rows)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Conv step: y for every token.  grid = (ceil(C / (8*CT)), ceil(T / TR), L*B)
+// with CT threads per block; each thread slides a 4-row window down TR tokens
+// for its 8 channels.
+constexpr int CONV_CT = 128;
+constexpr int CONV_TR = 8;
+
+template <int ACT>
+__global__ __launch_bounds__(CONV_CT) void conv_kernel(ConvParams p)
+{
+    const int lb = blockIdx.z;
+    const int b = lb % p.B;
+    if (p.active && p.active[b] == 0) return;
+    const int c0 = (blockIdx.x * CONV_CT + threadIdx.x) * 8;
+    if (c0 >= p.C) return;
+    const int t0 = blockIdx.y * CONV_TR;
+    const int l = lb / p.B;
+
+    float w[4][8], bias[8];
+    {
+        // conv_w[l][c][0..3] for 8 channels = 32 contiguous values.
+        float raw[32];
+        const size_t wi = (static_cast<size_t>(l) * p.C + c0) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) load_vec8<ACT>(p.conv_w, wi + 8 * q, raw + 8 * q);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j][c] = raw[c * 4 + j];
+    }
+    if (p.conv_b) {
+        load_vec8<ACT>(p.conv_b, static_cast<size_t>(l) * p.C + c0, bias);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) bias[c] = 0.0f;
+    }
+
+    // Window rows t0 .. t0+2 (rows < 3 live in conv_state).
+    float win[4][8];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        const int q = t0 + r;
+        if (q < 3)
+            load_vec8<ACT>(p.conv_state, (static_cast<size_t>(lb) * 3 + q) * p.C + c0, win[r]);
+        else
+            load_vec8<ACT>(p.x, (static_cast<size_t>(lb) * p.T + (q - 3)) * p.C + c0, win[r]);
+    }
+    const bool use_silu = (p.flags & FLAG_SILU) != 0;
+#pragma unroll
+    for (int i = 0; i < CONV_TR; ++i) {
+        const int t = t0 + i;
+        if (t >= p.T) break;
+        load_vec8<ACT>(p.x, (static_cast<size_t>(lb) * p.T + t) * p.C + c0, win[3]);
+        float yv[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float acc = w[0][c] * win[0][c];
+            acc = fmaf(w[1][c], win[1][c], acc);
+            acc = fmaf(w[2][c], win[2][c], acc);
+            acc = fmaf(w[3][c], win[3][c], acc);
+            acc += bias[c];
+            yv[c] = use_silu ? silu(acc) : acc;
+        }
+        store_vec8(p.y, (static_cast<size_t>(lb) * p.T + t) * p.C + c0, p.out, yv);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            win[0][c] = win[1][c];
+            win[1][c] = win[2][c];
+            win[2][c] = win[3][c];
+        }
+    }
+}
+
+hipError_t launch_conv(const ConvParams& p, hipStream_t s)
+{
+    const int gx = (p.C + 8 * CONV_CT - 1) / (8 * CONV_CT);
+    const int gy = (p.T + CONV_TR - 1) / CONV_TR;
+    const long long gz = static_cast<long long>(p.L) * p.B;
+    if (gy > 65535 || gz > 65535 || gz <= 0) return hipErrorInvalidConfiguration;
+    if (p.act == ACT_BF16)
+        hipLaunchKernelGGL(conv_kernel<ACT_BF16>, dim3(gx, gy, static_cast<unsigned>(gz)), dim3(CONV_CT),
+                           0, s, p);
+    else
+        hipLaunchKernelGGL(conv_kernel<ACT_F32>, dim3(gx, gy, static_cast<unsigned>(gz)), dim3(CONV_CT),
+                           0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,121 @@
+// gdn_internal.h -- kernel parameter blocks, launchers and small device
+// helpers shared by the HIP sources of libgdn.so.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+enum { ACT_F32 = 0, ACT_BF16 = 1 };
+enum { FLAG_SILU = 1u, FLAG_L2 = 2u };
+enum { ERR_KEEP = 1, ERR_SLOT = 2, ERR_INACTIVE_KEEP = 4 };
+
+// ---------------------------------------------------------------------------
+// Recurrent step kernel (verify and rewind share it, so that a rewind is
+// bit-identical to the verify candidate it replaces).
+enum RecMode { REC_VERIFY = 0, REC_REWIND = 1 };
+
+struct RecParams {
+    const void* x;
+    const void* conv_w;
+    const void* conv_b;
+    const void* conv_state;
+    const void* g;
+    const void* beta;
+    float* state;
+    const int32_t* cur;
+    void* o;
+    const uint8_t* active;
+    const int32_t* keep;
+    int32_t* err;
+    int32_t L, B, T, HV, HK, S, C;
+    int32_t act, out;
+    float scale, l2_eps;
+    uint32_t flags;
+    int32_t mode;
+    int32_t groups;     // L * B * HK
+    int32_t per_group;  // (HV / HK) * column slices per head
+};
+
+// ---------------------------------------------------------------------------
+// Conv-window shift (commit, rewind, conv_step with commit_state).
+enum WinMode { WIN_COMMIT = 0, WIN_REWIND = 1, WIN_FULL = 2 };
+
+struct WinParams {
+    const void* x;
+    void* conv_state;
+    int32_t* cur;
+    const int32_t* keep;
+    const uint8_t* active;
+    int32_t* err;
+    int32_t L, B, T, S, C;
+    int32_t act;
+    int32_t mode;
+};
+
+// ---------------------------------------------------------------------------
+// Standalone conv step (y over all tokens).
+struct ConvParams {
+    const void* x;
+    const void* conv_w;
+    const void* conv_b;
+    const void* conv_state;
+    void* y;
+    const uint8_t* active;
+    int32_t L, B, T, C;
+    int32_t act, out;
+    uint32_t flags;
+};
+
+hipError_t launch_recurrent(const RecParams& p, int DK, int DV, hipStream_t s);
+hipError_t launch_window(const WinParams& p, hipStream_t s);
+hipError_t launch_conv(const ConvParams& p, hipStream_t s);
+
+// Chunked prefill.
+struct PrefillParams {
+    const void* y;
+    const void* g;
+    const void* beta;
+    float* state;
+    const int32_t* cur;
+    void* o;
+    void* ws;
+    int32_t* err;
+    int32_t L, B, T, HV, HK, S, C;
+    int32_t act, out;
+    float scale, l2_eps;
+    uint32_t flags;
+};
+size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int chunk);
+hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Device helpers.
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t u)
+{
+    return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// float -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Activation element as fp32; ACT is a compile-time dtype so that loads are
+// never serialised behind a runtime dtype branch.
+template <int ACT>
+__device__ __forceinline__ float load_act(const void* base, size_t idx)
+{
+    if constexpr (ACT == ACT_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
+    else return static_cast<const float*>(base)[idx];
+}
+
+__device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
+
+}  // namespace gdn

@@ -1,0 +1,293 @@
+// gdn_recurrent.hip -- verify and rewind: fused short conv + SiLU + q/k L2
+// norm + T (<= 4) steps of the gated delta rule, one 64-lane wavefront per
+// (layer, row, value head, 32-column slice of the d_v axis).
+//
+// Method: "perf(qwen): full-context MTP draft prefill and replay-free rewind"
+// (Whallm PR #14), Summary item 4 -- rerun only the Gated DeltaNet mixer on
+// the captured verification inputs from the pre-verification state;
+// "Add request-owned eight-way MTP serving for Qwen 35B" (MTPLX PR #245),
+// What was broken items 2, 4, 6 -- B8/T2 verification, keep in {0,1,2},
+// keep=0 keeps the snapshot, rows are separable.  Update rule: gated delta
+// rule, S_t = a S_{t-1}(I - b k k^T) + b v k^T, o_t = S_t q_t, stored as
+// h = S^T (h[i][j], i over d_k, j over d_v contiguous).
+//
+// Why this shape on CDNA4: each (row, head) state is 64 KiB of fp32 that is
+// touched for only 3 * 2 * 128 * 128 flops per token, so the kernel is
+// bound by HBM.  The d_v columns of the state are independent recurrences
+// (column j only needs column j of h and v_j; k, q, a, b are shared), so a
+// head is cut into column slices with no communication between waves.
+// Inside a wave, lane (ig, j4) holds a float4 of 4 consecutive columns for
+// rows i = ig + IG*r: one load instruction covers IG rows x 128 contiguous
+// bytes, the whole slice is loaded once and kept in VGPRs across the T steps,
+// and the d_k reductions are in-lane sums plus a log2(IG)-level xor-shuffle
+// butterfly (every lane ends with bit-identical sums).  The two reductions
+// of a step (h^T k and h^T q) are taken together on the pre-update state and
+// the output uses o = scale*(a*(h^T q) + u*(k.q)), which equals
+// scale*h_t^T q algebraically.  The reduction tree does not depend on B, T,
+// the mode or the slot, so B8 == 8 x B1, prefix windows and rewind ==
+// candidate hold bit for bit.
+//
+// Workgroups are dispatched round-robin over the 8 XCDs; the block index is
+// remapped so that all waves of one (layer, row, qk head) -- which read the
+// same q/k conv channels -- land on the same XCD and share its L2.
+#include "gdn_internal.h"
+
+namespace gdn {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+template <int IG, int JL>
+__device__ __forceinline__ float sum_over_rows(float v)
+{
+#pragma unroll
+    for (int off = JL; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <int DK, int DV, int ACT>
+__global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
+{
+    constexpr int SW = DV < 32 ? DV : 32;  // columns per wave
+    constexpr int NS = DV / SW;            // column slices per head
+    constexpr int JL = SW / 4;             // lanes across one row segment
+    constexpr int IG = 64 / JL;            // row groups per wave
+    constexpr int RPL = DK / IG;           // rows held per lane
+    constexpr int NCH = 2 * DK + SW;       // conv channels this wave needs
+    static_assert(RPL >= 1 && DK % IG == 0, "tile shape");
+
+    __shared__ float ys[4][NCH];
+
+    // ---- block -> (layer, row, qk head, value head, slice), XCD-aware ----
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7;
+    const int sgrp = bid >> 3;
+    const int r_in = sgrp % p.per_group;
+    const int grp = (sgrp / p.per_group) * 8 + xcd;
+    if (grp >= p.groups) return;
+    const int m = grp % p.HK;
+    const int lb = grp / p.HK;  // l * B + b
+    const int b = lb % p.B;
+    const int gsz = p.HV / p.HK;
+    const int slice = r_in % NS;
+    const int hv = m * gsz + r_in / NS;
+
+    const int lane = threadIdx.x;
+    const int j4 = lane % JL;
+    const int ig = lane / JL;
+    const int col0 = slice * SW + j4 * 4;
+
+    // ---- row status ----
+    int slot0 = 0, is_active = 1, kp = 0;
+    if (p.cur) slot0 = p.cur[lb];
+    if (p.active) is_active = p.active[b];
+    if (p.keep) kp = p.keep[b];
+    int nsteps = p.T;
+    if (p.mode == REC_VERIFY) {
+        if (is_active == 0) return;
+        if (slot0 < 0 || slot0 >= p.S) {
+            if (lane == 0 && p.err) atomicOr(p.err, ERR_SLOT);
+            return;
+        }
+    } else {
+        int e = 0;
+        if (kp < 0 || kp > p.T) e |= ERR_KEEP;
+        if (slot0 < 0 || slot0 >= p.S) e |= ERR_SLOT;
+        if (e) {
+            if (lane == 0 && p.err) atomicOr(p.err, e);
+            return;
+        }
+        if (kp == 0) return;
+        nsteps = kp;
+    }
+
+    // ---- conv inputs: q and k channels of qk head m, v channels of the slice.
+    // Every load is unconditional (lanes past the last channel re-read it,
+    // rows past the window re-read its last row, a missing bias reads a
+    // weight and discards it) so that they are all in flight together.
+    const int C = p.C;
+    const int l = lb / p.B;
+    const size_t xrow = static_cast<size_t>(lb) * p.T;        // x row of token 0
+    const size_t srow = static_cast<size_t>(lb) * 3;          // conv_state row 0
+    const bool has_bias = p.conv_b != nullptr;
+    const void* bptr = has_bias ? p.conv_b : p.conv_w;
+    constexpr int NG = (NCH + 63) / 64;
+    float wv[NG][4];
+    float win[NG][7];
+    float bias[NG];
+#pragma unroll
+    for (int n = 0; n < NG; ++n) {
+        const int ch = min(lane + 64 * n, NCH - 1);
+        const int c = ch < DK ? m * DK + ch
+                    : (ch < 2 * DK ? p.HK * DK + m * DK + (ch - DK)
+                                   : 2 * p.HK * DK + hv * DV + slice * SW + (ch - 2 * DK));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            wv[n][j] = load_act<ACT>(p.conv_w, (static_cast<size_t>(l) * C + c) * 4 + j);
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+            win[n][r] = load_act<ACT>(p.conv_state, (srow + r) * C + c);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            win[n][3 + t] = load_act<ACT>(p.x, (xrow + min(t, p.T - 1)) * C + c);
+        const float bv = load_act<ACT>(bptr, has_bias ? static_cast<size_t>(l) * C + c : 0);
+        bias[n] = has_bias ? bv : 0.0f;
+    }
+    // Gates of every window token (rows past the window re-read the last one).
+    const size_t ghead = xrow * p.HV + hv;  // g/beta index of token 0
+    float gate_a[4], gate_b[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const size_t gi = ghead + static_cast<size_t>(min(t, p.T - 1)) * p.HV;
+        gate_a[t] = load_act<ACT>(p.g, gi);
+        gate_b[t] = load_act<ACT>(p.beta, gi);
+    }
+
+    // ---- the state slice: every load issued before any use ----
+    const size_t tile = static_cast<size_t>(DK) * DV;
+    float* st_lb = p.state + static_cast<size_t>(lb) * p.S * p.HV * tile;
+    const float* src = st_lb + (static_cast<size_t>(slot0) * p.HV + hv) * tile + col0;
+    f4 h[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+        h[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src + (ig + IG * r) * DV));
+
+    // ---- conv + SiLU for every window token, into LDS ----
+    const bool use_silu = (p.flags & FLAG_SILU) != 0;
+#pragma unroll
+    for (int n = 0; n < NG; ++n) {
+        const int ch = lane + 64 * n;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float acc = wv[n][0] * win[n][t];
+            acc = fmaf(wv[n][1], win[n][t + 1], acc);
+            acc = fmaf(wv[n][2], win[n][t + 2], acc);
+            acc = fmaf(wv[n][3], win[n][t + 3], acc);
+            acc += bias[n];
+            const float sv = silu(acc);
+            if (ch < NCH && t < nsteps) ys[t][ch] = use_silu ? sv : acc;
+        }
+    }
+    __syncthreads();
+
+    const bool l2 = (p.flags & FLAG_L2) != 0;
+    for (int t = 0; t < nsteps; ++t) {
+        float kr[RPL], qr[RPL];
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            qr[r] = ys[t][ig + IG * r];
+            kr[r] = ys[t][DK + ig + IG * r];
+        }
+        float pp[4] = {0.f, 0.f, 0.f, 0.f}, rr[4] = {0.f, 0.f, 0.f, 0.f};
+        float sq = 0.f, sk = 0.f, kq = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                pp[c] = fmaf(h[r][c], kr[r], pp[c]);
+                rr[c] = fmaf(h[r][c], qr[r], rr[c]);
+            }
+            sq = fmaf(qr[r], qr[r], sq);
+            sk = fmaf(kr[r], kr[r], sk);
+            kq = fmaf(kr[r], qr[r], kq);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            pp[c] = sum_over_rows<IG, JL>(pp[c]);
+            rr[c] = sum_over_rows<IG, JL>(rr[c]);
+        }
+        sq = sum_over_rows<IG, JL>(sq);
+        sk = sum_over_rows<IG, JL>(sk);
+        kq = sum_over_rows<IG, JL>(kq);
+
+        const float inv_nq = l2 ? 1.0f / sqrtf(sq + p.l2_eps) : 1.0f;
+        const float inv_nk = l2 ? 1.0f / sqrtf(sk + p.l2_eps) : 1.0f;
+        const float kqn = kq * inv_nk * inv_nq;
+        // t is uniform: select the token's gates without dynamic indexing.
+        const float gt = t == 0 ? gate_a[0] : t == 1 ? gate_a[1] : t == 2 ? gate_a[2] : gate_a[3];
+        const float bt = t == 0 ? gate_b[0] : t == 1 ? gate_b[1] : t == 2 ? gate_b[2] : gate_b[3];
+        const float a = expf(gt);
+
+        float u[4], oo[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float vj = ys[t][2 * DK + j4 * 4 + c];
+            u[c] = bt * (vj - a * (pp[c] * inv_nk));
+            oo[c] = p.scale * (a * (rr[c] * inv_nq) + u[c] * kqn);
+        }
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const float kn = kr[r] * inv_nk;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) h[r][c] = fmaf(a, h[r][c], kn * u[c]);
+        }
+
+        if (p.o && ig == 0) {
+            const size_t oi = ((xrow + t) * p.HV + hv) * DV + col0;
+            if (p.out == ACT_BF16) {
+                uint2 pk;
+                pk.x = f32_to_bf16_bits(oo[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(oo[1])) << 16);
+                pk.y = f32_to_bf16_bits(oo[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(oo[3])) << 16);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.o) + oi) = pk;
+            } else {
+                f4 ov = {oo[0], oo[1], oo[2], oo[3]};
+                __builtin_nontemporal_store(ov, reinterpret_cast<f4*>(static_cast<float*>(p.o) + oi));
+            }
+        }
+        if (p.mode == REC_VERIFY) {
+            const int slot = (slot0 + t + 1) % p.S;
+            float* dst = st_lb + (static_cast<size_t>(slot) * p.HV + hv) * tile + col0;
+#pragma unroll
+            for (int r = 0; r < RPL; ++r)
+                __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(dst + (ig + IG * r) * DV));
+        }
+    }
+    if (p.mode == REC_REWIND) {
+        float* dst = st_lb + (static_cast<size_t>(slot0) * p.HV + hv) * tile + col0;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r)
+            __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(dst + (ig + IG * r) * DV));
+    }
+}
+
+template <int DK, int DV>
+static hipError_t launch_rec(RecParams p, hipStream_t s)
+{
+    constexpr int SW = DV < 32 ? DV : 32;
+    constexpr int NS = DV / SW;
+    p.groups = p.L * p.B * p.HK;
+    p.per_group = (p.HV / p.HK) * NS;
+    const long long blocks = static_cast<long long>((p.groups + 7) / 8) * 8 * p.per_group;
+    if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (p.act == ACT_BF16)
+        hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_BF16>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(64), 0, s, p);
+    else
+        hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_F32>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int DK>
+static hipError_t launch_rec_dv(const RecParams& p, int DV, hipStream_t s)
+{
+    switch (DV) {
+    case 16: return launch_rec<DK, 16>(p, s);
+    case 32: return launch_rec<DK, 32>(p, s);
+    case 64: return launch_rec<DK, 64>(p, s);
+    case 128: return launch_rec<DK, 128>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_recurrent(const RecParams& p, int DK, int DV, hipStream_t s)
+{
+    switch (DK) {
+    case 16: return launch_rec_dv<16>(p, DV, s);
+    case 32: return launch_rec_dv<32>(p, DV, s);
+    case 64: return launch_rec_dv<64>(p, DV, s);
+    case 128: return launch_rec_dv<128>(p, DV, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace gdn

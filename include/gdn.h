@@ -1,0 +1,178 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the Gated DeltaNet verify / commit / rewind /
+ * conv-step / chunked-prefill path of speculative multi-token-prediction
+ * (MTP) decoding, as hand-written HIP kernels for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Page sources (title, then section):
+ *  [P1] "perf(qwen): full-context MTP draft prefill and replay-free rewind"
+ *       (Whallm PR #14): Summary item 4 (replay-free rollback: rerun only the
+ *       Gated DeltaNet mixer on the captured verification inputs from the
+ *       pre-verification state); Measurements (1,024-token layer-major
+ *       prefill calls); Tests (rewind equals a direct forward over the
+ *       accepted prefix).
+ *  [P2] "MTP inference: review and commit structure" (eole docs):
+ *       Functional commits items 2 and 4 (verifier buffers, accepted-prefix
+ *       state replay, grouped copies, short convolution with a mutated
+ *       convolution cache); Review fixes (grouped replay checks every shape,
+ *       dtype and device before combining layers); Verification and limits
+ *       (chunked recurrence differs from the sequential one only in rounding).
+ *  [P3] "Add request-owned eight-way MTP serving for Qwen 35B" (MTPLX PR
+ *       #245): What was broken item 2 (a row commits two, one or no tokens;
+ *       inactive rows use keep=0 and keep their pre-verification recurrent
+ *       state), item 4 (keep=0 restores the snapshotted base state), item 6
+ *       (a fixed B8/T2 cohort; the grid grows to 8 x 32 head rows; rows are
+ *       separable); Clean-install verification (fail closed, no fallback).
+ * The recurrence is the gated delta rule (Yang, Kautz, Hatamizadeh, "Gated
+ * Delta Networks", ICLR 2025):
+ *     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T,  o_t = S_t q_t
+ * stored transposed: h = S^T, h[i][j], i over d_k, j over d_v (contiguous).
+ *
+ * CONVENTIONS (every entry point)
+ *  - Every array argument is a caller-owned DEVICE pointer, 16-byte aligned,
+ *    dense, row-major in the layout given below.  The library never
+ *    allocates, frees or synchronises inside a call; it launches on `stream`
+ *    (a hipStream_t; NULL = the legacy default stream) and returns.
+ *  - Host-side validation runs before anything is launched.  On any failure
+ *    a status other than GDN_OK is returned and nothing is launched.
+ *  - Data errors found on the device (keep or slot out of range, keep != 0
+ *    on an inactive row) leave that (layer, row) untouched and OR a
+ *    GDN_ERR_* bit into *err when err is not NULL.  The library never
+ *    clears *err.
+ *  - Outputs (o, y, workspace) must not alias any input.
+ *  - The library holds no per-call global state: calls on distinct streams
+ *    over disjoint buffers are independent.
+ *
+ * SHAPES (C = 2*HK*DK + HV*DV conv channels ordered [q heads | k heads |
+ * v heads]; value head h reads qk head h / (HV/HK))
+ *   x, y        [L][B][T][C]          act dtype
+ *   conv_w      [L][C][KCONV]         act dtype (tap KCONV-1 hits the newest token)
+ *   conv_b      [L][C] or NULL        act dtype
+ *   conv_state  [L][B][KCONV-1][C]    act dtype (row 0 is the oldest)
+ *   g, beta     [L][B][T][HV]         act dtype; a = exp(g) (g <= 0), beta in [0,1]
+ *   state       [L][B][S][HV][DK][DV] float32, S ring slots per (layer, row)
+ *   cur         [L][B] int32          committed slot; NULL means slot 0
+ *   o           [L][B][T][HV][DV]     out dtype
+ *   active      [B] uint8             NULL means every row is active
+ *   keep        [B] int32             tokens to commit per row, 0..T
+ *   err         [1] int32 or NULL
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_E_NULL = 1,        /* a required pointer is NULL */
+    GDN_E_SHAPE = 2,       /* a size is out of the supported range */
+    GDN_E_DTYPE = 3,       /* act/out is not GDN_F32 or GDN_BF16 */
+    GDN_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    GDN_E_UNSUPPORTED = 5, /* a valid request this build does not implement */
+    GDN_E_WORKSPACE = 6,   /* workspace NULL or smaller than gdn_workspace_size */
+    GDN_E_HIP = 7          /* the HIP runtime reported a launch failure */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+#define GDN_FLAG_CONV_SILU 1u /* SiLU after the conv */
+#define GDN_FLAG_QK_L2NORM 2u /* q, k divided by sqrt(sum of squares + l2_eps) per qk head */
+
+#define GDN_ERR_KEEP 1          /* keep[b] outside 0..T */
+#define GDN_ERR_SLOT 2          /* cur[l][b] outside 0..S-1 */
+#define GDN_ERR_INACTIVE_KEEP 4 /* keep[b] != 0 on an inactive row */
+
+typedef struct {
+    int32_t L, B, T;        /* layers, rows, tokens per call */
+    int32_t HV, HK;         /* value heads, qk heads (HV % HK == 0) */
+    int32_t DK, DV;         /* head dims, each one of 16, 32, 64, 128 */
+    int32_t KCONV;          /* conv width; must be 4 */
+    int32_t S;              /* state ring slots per (layer, row) */
+    int32_t act, out;       /* gdn_dtype of activations / of o and y */
+    float scale, l2_eps;    /* output scale; eps of the q/k L2 norm */
+    uint32_t flags;         /* GDN_FLAG_* */
+} gdn_dims;
+
+/* Short causal depthwise conv (+ SiLU) over every token of every active row
+ * ([P2] Functional commits 2 and 4): y[t][c] = act(sum_j w[c][j] W[t+j][c]
+ * + b[c]) with the window W = [conv_state ; x].  If commit_state != 0 the
+ * conv cache of each active row becomes the last KCONV-1 window rows.
+ * Writes y (out dtype) and, if asked, conv_state; inactive rows are not
+ * touched.  Used for decode (T=1) and for prompt prefill (e.g. T=1024). */
+gdn_status gdn_conv_step(const gdn_dims* d, const void* x, const void* conv_w,
+                         const void* conv_b, void* conv_state, void* y,
+                         const uint8_t* active, int commit_state, int32_t* err,
+                         void* stream);
+
+/* Verify a window of T <= 4 tokens ([P3] What was broken items 2, 4, 6;
+ * [P1] Summary item 4): for each active row, conv + SiLU + q/k L2 norm on
+ * the window, then T steps of the gated delta rule from slot cur.  The state
+ * after token t (t = 0..T-1) is written to slot (cur + t + 1) mod S and the
+ * token's output to o[t].  Slot cur (the pre-verification snapshot),
+ * conv_state and cur are never written, so any keep in 0..T can be
+ * committed afterwards.  Requires S >= T + 1.  Inactive rows write nothing.
+ * err: GDN_ERR_SLOT. */
+gdn_status gdn_verify(const gdn_dims* d, const void* x, const void* conv_w,
+                      const void* conv_b, const void* conv_state, const void* g,
+                      const void* beta, float* state, const int32_t* cur, void* o,
+                      const uint8_t* active, int32_t* err, void* stream);
+
+/* Commit each row's accepted length after gdn_verify ([P3] What was broken
+ * items 2 and 4): for active rows with keep >= 1, cur <- (cur + keep) mod S
+ * (the candidate slot becomes the committed state, no copy) and conv_state
+ * <- window rows keep .. keep+KCONV-2 of [conv_state ; x].  keep = 0 and
+ * inactive rows write nothing, so the snapshot stays bit-identical.  x and
+ * the dims must be those given to gdn_verify.  Requires S >= T + 1.
+ * err: GDN_ERR_KEEP, GDN_ERR_SLOT, GDN_ERR_INACTIVE_KEEP. */
+gdn_status gdn_commit(const gdn_dims* d, const void* x, void* conv_state, int32_t* cur,
+                      const int32_t* keep, const uint8_t* active, int32_t* err,
+                      void* stream);
+
+/* Replay-free rewind ([P1] Summary item 4; [P2] Verification and limits:
+ * partial commits replay only the accepted recurrent prefix; Review fixes:
+ * grouped replay over layers): for each row with keep >= 1, rerun conv +
+ * recurrence over the first keep captured window tokens (x, g, beta of the
+ * verification, T <= 4) starting from slot cur, write the result back into
+ * slot cur in place and commit the conv cache as gdn_commit does.  cur is
+ * not changed.  keep = 0 touches nothing.  o may be NULL; when given, o[t]
+ * is written for t < keep.  Bit-identical to gdn_verify's candidate keep.
+ * err: GDN_ERR_KEEP, GDN_ERR_SLOT. */
+gdn_status gdn_rewind(const gdn_dims* d, const void* x, const void* conv_w,
+                      const void* conv_b, void* conv_state, const void* g,
+                      const void* beta, float* state, const int32_t* cur,
+                      const int32_t* keep, void* o, int32_t* err, void* stream);
+
+/* Chunked prompt prefill of the same recurrence ([P1] Measurements:
+ * 1,024-token layer-major prefill calls; [P2] Verification and limits: the
+ * chunk recurrence equals the sequential one up to rounding).  y holds the
+ * post-conv q|k|v channels (as written by gdn_conv_step); q and k are
+ * L2-normalised here when GDN_FLAG_QK_L2NORM is set.  Every row's state in
+ * slot cur is advanced over all T tokens in place, and o[t] is written for
+ * every token.  chunk must be 64; chunks restart at each call's first token
+ * and the last one may be short.  workspace: device scratch of at least
+ * gdn_workspace_size(d, chunk) bytes, owned by the caller, clobbered.
+ * err: GDN_ERR_SLOT. */
+gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* y, const void* g,
+                               const void* beta, float* state, const int32_t* cur, void* o,
+                               int32_t chunk, void* workspace, size_t workspace_bytes,
+                               int32_t* err, void* stream);
+
+/* Workspace bytes gdn_prefill_chunked needs for these dims (0 on bad dims). */
+size_t gdn_workspace_size(const gdn_dims* d, int32_t chunk);
+
+/* Static, human-readable name of a status. */
+const char* gdn_status_string(gdn_status s);
+
+/* Build identification: library version and target architecture. */
+const char* gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads,
+exports every symbol include/gdn.h declares, and host validation rejects bad
+arguments before any HIP call (fail closed, as on "Add request-owned
+eight-way MTP serving for Qwen 35B", Clean-install verification; shapes
+checked before work, as on "MTP inference: review and commit structure",
+Review fixes)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+LIB = os.path.join(ROOT, "gated_deltanet_recurrence_conv_amd", "libgdn.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from gated_deltanet_recurrence_conv_amd import build
+        build.build()
+    return ctypes.CDLL(LIB)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:gdn_status|size_t|const char\*)\s+(gdn_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_prefill_chunked",
+              "gdn_workspace_size", "gdn_status_string", "gdn_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_binding_exports_same_names():
+    from gated_deltanet_recurrence_conv_amd import binding
+    for n in declared_functions():
+        assert hasattr(binding, n), n
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("B", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("HV", ctypes.c_int32), ("HK", ctypes.c_int32), ("DK", ctypes.c_int32),
+                ("DV", ctypes.c_int32), ("KCONV", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("out", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("l2_eps", ctypes.c_float),
+                ("flags", ctypes.c_uint32)]
+
+
+def good():
+    return Dims(1, 8, 2, 32, 16, 128, 128, 4, 3, 1, 0, 1.0, 1e-6, 3)
+
+
+FAKE = 1 << 20   # aligned, never dereferenced: validation fails before any launch
+
+
+def verify_call(lib, d, **over):
+    args = dict(x=FAKE, w=FAKE, b=None, cs=FAKE, g=FAKE, beta=FAKE, st=FAKE, cur=None, o=FAKE,
+                act=None, err=None)
+    args.update(over)
+    f = lib.gdn_verify
+    f.argtypes = [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 12
+    return f(ctypes.byref(d), args["x"], args["w"], args["b"], args["cs"], args["g"],
+             args["beta"], args["st"], args["cur"], args["o"], args["act"], args["err"], None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("act", 7, 3), ("out", -1, 3), ("L", 0, 2), ("B", 0, 2), ("T", 0, 2), ("T", 5, 2),
+    ("HV", 30, 2), ("DK", 96, 2), ("DV", 8, 2), ("KCONV", 3, 2), ("S", 2, 2)])
+def test_verify_rejects_bad_dims(lib, field, value, status):
+    d = good()
+    setattr(d, field, value)
+    assert verify_call(lib, d) == status
+
+
+def test_verify_rejects_null_and_misaligned(lib):
+    assert verify_call(lib, good(), x=None) == 1
+    assert verify_call(lib, good(), o=None) == 1
+    assert verify_call(lib, good(), st=FAKE + 4) == 4
+    assert verify_call(lib, good(), cur=FAKE + 8) == 4
+    f = lib.gdn_verify
+    f.argtypes = [ctypes.c_void_p] * 13
+    assert f(None, *([FAKE] * 12)) == 1
+
+
+def test_commit_rewind_conv_prefill_validation(lib):
+    d = good()
+    lib.gdn_commit.argtypes = [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 7
+    assert lib.gdn_commit(ctypes.byref(d), FAKE, FAKE, None, FAKE, None, None, None) == 1
+    d.T = 3   # S = 3 < T + 1
+    assert lib.gdn_commit(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None) == 2
+    d = good()
+    lib.gdn_rewind.argtypes = [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 12
+    assert lib.gdn_rewind(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None,
+                          None, None, None, None) == 1          # keep missing
+    lib.gdn_conv_step.argtypes = [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 6 + \
+        [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    d.T = 1024
+    assert lib.gdn_conv_step(ctypes.byref(d), FAKE, FAKE, None, FAKE, None, None, 1, None,
+                             None) == 1
+    d.act = 5
+    assert lib.gdn_conv_step(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, None, 1, None,
+                             None) == 3
+    d = good()
+    d.T = 1024
+    lib.gdn_prefill_chunked.argtypes = [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 6 + \
+        [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.gdn_prefill_chunked(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, 32,
+                                   None, 0, None, None) == 2    # chunk must be 64
+    lib.gdn_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
+    lib.gdn_workspace_size.restype = ctypes.c_size_t
+    assert lib.gdn_workspace_size(ctypes.byref(d), 32) == 0
+
+
+def test_status_strings_and_version(lib):
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_version.restype = ctypes.c_char_p
+    for s in range(8):
+        assert lib.gdn_status_string(s).startswith(b"GDN_")
+    assert b"gfx950" in lib.gdn_version()
