@@ -40,7 +40,22 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (used to "
+                         "calibrate the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_probe(torch):
+    n = 1 << 28                     # 2^28 fp32 = 1 GiB
+    a = torch.randn(n, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "copies": 3}), flush=True)
 
 
 def log(msg):
@@ -353,6 +368,9 @@ def main():
     from gated_deltanet_recurrence_conv_amd import workloads as W
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        copy_probe(torch)
+        return
     log("bench: %s on %s" % (gb.gdn_version(), torch.cuda.get_device_name(0)))
     log("bench: headline B8/T2 cohort x %d layers, %d steps" % (L_POOL, args.steps))
     h = headline(torch, gb, W, args)

@@ -21,6 +21,13 @@ if not os.path.exists(LIB_PATH):
                       "`python -m gated_deltanet_recurrence_conv_amd.build` -- there is no "
                       "fallback path" % LIB_PATH)
 
+# PyTorch ships its own HIP runtime (SONAME libamdhip64.so.7).  Importing
+# torch first makes the dynamic loader bind libgdn.so to that same runtime, so
+# the process has one HIP runtime and torch's device memory and streams are
+# valid in libgdn's calls.  Loading libgdn.so first would pull in a second
+# runtime that sees no device.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 GDN_OK = 0
@@ -56,7 +63,10 @@ class GdnError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         msg = _lib.gdn_status_string(status)
-        super().__init__("%s: %s" % (where, msg.decode() if msg else STATUS_NAMES.get(status)))
+        text = "%s: %s" % (where, msg.decode() if msg else STATUS_NAMES.get(status))
+        if status == 7:
+            text += " (%s)" % _lib.gdn_last_hip_error().decode()
+        super().__init__(text)
 
 
 _vp, _i32 = ctypes.c_void_p, ctypes.c_int32
@@ -73,11 +83,13 @@ _lib.gdn_status_string.argtypes = [ctypes.c_int]
 _lib.gdn_status_string.restype = ctypes.c_char_p
 _lib.gdn_version.argtypes = []
 _lib.gdn_version.restype = ctypes.c_char_p
+_lib.gdn_last_hip_error.argtypes = []
+_lib.gdn_last_hip_error.restype = ctypes.c_char_p
 for _n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_prefill_chunked"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_prefill_chunked",
-            "gdn_workspace_size", "gdn_status_string", "gdn_version")
+            "gdn_workspace_size", "gdn_status_string", "gdn_version", "gdn_last_hip_error")
 
 
 def _torch():
@@ -221,6 +233,10 @@ def gdn_status_string(status: int) -> str:
 
 def gdn_version() -> str:
     return _lib.gdn_version().decode()
+
+
+def gdn_last_hip_error() -> str:
+    return _lib.gdn_last_hip_error().decode()
 
 
 def raw_library():

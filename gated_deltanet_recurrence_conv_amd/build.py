@@ -32,7 +32,8 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-mcode-object-version=5", "-O3", "-std=c++17",
+           "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp] + srcs

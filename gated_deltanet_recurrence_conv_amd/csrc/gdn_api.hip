@@ -44,7 +44,13 @@ gdn_status check_dims(const gdn_dims* d)
     return GDN_OK;
 }
 
-gdn_status check_ptrs(std::initializer_list<const void*> req, std::initializer_list<const void*> opt)
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Tensor arguments (req / opt) must be 16-byte aligned, since the kernels
+// move them in 16-byte vectors; the small per-row int32 arrays (cur, keep,
+// err: ints4) only need their natural 4-byte alignment.
+gdn_status check_ptrs(std::initializer_list<const void*> req, std::initializer_list<const void*> opt,
+                      std::initializer_list<const void*> ints4 = {})
 {
     for (const void* p : req)
         if (!p) return GDN_E_NULL;
@@ -52,10 +58,20 @@ gdn_status check_ptrs(std::initializer_list<const void*> req, std::initializer_l
         if (!aligned(p)) return GDN_E_ALIGN;
     for (const void* p : opt)
         if (p && !aligned(p)) return GDN_E_ALIGN;
+    for (const void* p : ints4)
+        if (p && !aligned4(p)) return GDN_E_ALIGN;
     return GDN_OK;
 }
 
-gdn_status from_hip(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_E_HIP; }
+// The HIP error behind the most recent GDN_E_HIP of this thread.
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+gdn_status from_hip(hipError_t e)
+{
+    if (e == hipSuccess) return GDN_OK;
+    g_last_hip_error = e;
+    return GDN_E_HIP;
+}
 
 RecParams rec_params(const gdn_dims* d)
 {
@@ -78,7 +94,7 @@ const char* gdn_status_string(gdn_status s)
     case GDN_E_NULL: return "GDN_E_NULL: a required pointer is NULL";
     case GDN_E_SHAPE: return "GDN_E_SHAPE: a size is outside the supported range";
     case GDN_E_DTYPE: return "GDN_E_DTYPE: act/out must be GDN_F32 or GDN_BF16";
-    case GDN_E_ALIGN: return "GDN_E_ALIGN: a pointer is not 16-byte aligned";
+    case GDN_E_ALIGN: return "GDN_E_ALIGN: a tensor is not 16-byte aligned or an int32 array not 4-byte aligned";
     case GDN_E_UNSUPPORTED: return "GDN_E_UNSUPPORTED: not implemented for these arguments";
     case GDN_E_WORKSPACE: return "GDN_E_WORKSPACE: workspace missing or too small";
     case GDN_E_HIP: return "GDN_E_HIP: the HIP runtime reported a launch failure";
@@ -88,13 +104,18 @@ const char* gdn_status_string(gdn_status s)
 
 const char* gdn_version(void) { return "libgdn 0.1.0 (HIP, gfx950)"; }
 
+const char* gdn_last_hip_error(void)
+{
+    return g_last_hip_error == hipSuccess ? "" : hipGetErrorString(g_last_hip_error);
+}
+
 gdn_status gdn_conv_step(const gdn_dims* d, const void* x, const void* conv_w, const void* conv_b,
                          void* conv_state, void* y, const uint8_t* active, int commit_state,
                          int32_t* err, void* stream)
 {
     gdn_status st = check_dims(d);
     if (st != GDN_OK) return st;
-    st = check_ptrs({x, conv_w, conv_state, y}, {conv_b, err});
+    st = check_ptrs({x, conv_w, conv_state, y}, {conv_b}, {err});
     if (st != GDN_OK) return st;
     (void)err;
     ConvParams p{};
@@ -120,7 +141,7 @@ gdn_status gdn_verify(const gdn_dims* d, const void* x, const void* conv_w, cons
     gdn_status st = check_dims(d);
     if (st != GDN_OK) return st;
     if (d->T > 4 || d->S < d->T + 1) return GDN_E_SHAPE;
-    st = check_ptrs({x, conv_w, conv_state, g, beta, state, o}, {conv_b, cur, err});
+    st = check_ptrs({x, conv_w, conv_state, g, beta, state, o}, {conv_b}, {cur, err});
     if (st != GDN_OK) return st;
     RecParams p = rec_params(d);
     p.x = x; p.conv_w = conv_w; p.conv_b = conv_b; p.conv_state = conv_state;
@@ -135,7 +156,8 @@ gdn_status gdn_commit(const gdn_dims* d, const void* x, void* conv_state, int32_
     gdn_status st = check_dims(d);
     if (st != GDN_OK) return st;
     if (d->T > 4 || d->S < d->T + 1) return GDN_E_SHAPE;
-    st = check_ptrs({x, conv_state, cur, keep}, {err});
+    if (!cur || !keep) return GDN_E_NULL;
+    st = check_ptrs({x, conv_state}, {}, {cur, keep, err});
     if (st != GDN_OK) return st;
     WinParams w{};
     w.x = x; w.conv_state = conv_state; w.cur = cur; w.keep = keep; w.active = active;
@@ -152,7 +174,8 @@ gdn_status gdn_rewind(const gdn_dims* d, const void* x, const void* conv_w, cons
     gdn_status st = check_dims(d);
     if (st != GDN_OK) return st;
     if (d->T > 4) return GDN_E_SHAPE;
-    st = check_ptrs({x, conv_w, conv_state, g, beta, state, keep}, {conv_b, cur, o, err});
+    if (!keep) return GDN_E_NULL;
+    st = check_ptrs({x, conv_w, conv_state, g, beta, state}, {conv_b, o}, {cur, keep, err});
     if (st != GDN_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     RecParams p = rec_params(d);
@@ -184,7 +207,7 @@ gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* y, const void* g, 
     gdn_status st = check_dims(d);
     if (st != GDN_OK) return st;
     if (chunk != 64) return GDN_E_SHAPE;
-    st = check_ptrs({y, g, beta, state, o}, {cur, err, workspace});
+    st = check_ptrs({y, g, beta, state, o}, {workspace}, {cur, err});
     if (st != GDN_OK) return st;
     const size_t need = gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, chunk);
     if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;

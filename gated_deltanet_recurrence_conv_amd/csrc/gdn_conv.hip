@@ -117,6 +117,7 @@ hipError_t launch_window(const WinParams& p, hipStream_t s)
     const int per_row = (p.C + 8 * 256 - 1) / (8 * 256);
     const long long rows = static_cast<long long>(p.L) * p.B;
     if (rows > 65535 || rows <= 0) return hipErrorInvalidConfiguration;
+    clear_stale_error();
     hipLaunchKernelGGL(window_kernel, dim3(per_row, static_cast<unsigned>(rows)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
@@ -200,6 +201,7 @@ hipError_t launch_conv(const ConvParams& p, hipStream_t s)
     const int gy = (p.T + CONV_TR - 1) / CONV_TR;
     const long long gz = static_cast<long long>(p.L) * p.B;
     if (gy > 65535 || gz > 65535 || gz <= 0) return hipErrorInvalidConfiguration;
+    clear_stale_error();
     if (p.act == ACT_BF16)
         hipLaunchKernelGGL(conv_kernel<ACT_BF16>, dim3(gx, gy, static_cast<unsigned>(gz)), dim3(CONV_CT),
                            0, s, p);

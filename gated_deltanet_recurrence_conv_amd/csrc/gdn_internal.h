@@ -69,6 +69,10 @@ struct ConvParams {
     uint32_t flags;
 };
 
+// Drops an error a previous runtime call may have left behind, so that the
+// status read right after a launch belongs to that launch.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
 hipError_t launch_recurrent(const RecParams& p, int DK, int DV, hipStream_t s);
 hipError_t launch_window(const WinParams& p, hipStream_t s);
 hipError_t launch_conv(const ConvParams& p, hipStream_t s);

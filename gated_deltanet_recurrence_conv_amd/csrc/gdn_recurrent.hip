@@ -258,6 +258,7 @@ static hipError_t launch_rec(RecParams p, hipStream_t s)
     p.per_group = (p.HV / p.HK) * NS;
     const long long blocks = static_cast<long long>((p.groups + 7) / 8) * 8 * p.per_group;
     if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    clear_stale_error();
     if (p.act == ACT_BF16)
         hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_BF16>), dim3(static_cast<unsigned>(blocks)),
                            dim3(64), 0, s, p);

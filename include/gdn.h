@@ -29,8 +29,10 @@
  * stored transposed: h = S^T, h[i][j], i over d_k, j over d_v (contiguous).
  *
  * CONVENTIONS (every entry point)
- *  - Every array argument is a caller-owned DEVICE pointer, 16-byte aligned,
- *    dense, row-major in the layout given below.  The library never
+ *  - Every array argument is a caller-owned DEVICE pointer, dense, row-major
+ *    in the layout given below.  Tensors (x, y, conv_w, conv_b, conv_state,
+ *    g, beta, state, o, workspace) must be 16-byte aligned; the int32 arrays
+ *    cur, keep and err 4-byte aligned; active has no alignment rule.  The library never
  *    allocates, frees or synchronises inside a call; it launches on `stream`
  *    (a hipStream_t; NULL = the legacy default stream) and returns.
  *  - Host-side validation runs before anything is launched.  On any failure
@@ -72,7 +74,7 @@ typedef enum {
     GDN_E_NULL = 1,        /* a required pointer is NULL */
     GDN_E_SHAPE = 2,       /* a size is out of the supported range */
     GDN_E_DTYPE = 3,       /* act/out is not GDN_F32 or GDN_BF16 */
-    GDN_E_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    GDN_E_ALIGN = 4,       /* a pointer breaks the alignment rule above */
     GDN_E_UNSUPPORTED = 5, /* a valid request this build does not implement */
     GDN_E_WORKSPACE = 6,   /* workspace NULL or smaller than gdn_workspace_size */
     GDN_E_HIP = 7          /* the HIP runtime reported a launch failure */
@@ -170,6 +172,10 @@ const char* gdn_status_string(gdn_status s);
 
 /* Build identification: library version and target architecture. */
 const char* gdn_version(void);
+
+/* Text of the HIP runtime error behind this thread's most recent GDN_E_HIP
+ * ("" if there was none).  Static storage; never NULL. */
+const char* gdn_last_hip_error(void);
 
 #ifdef __cplusplus
 }

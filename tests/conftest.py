@@ -10,5 +10,11 @@ for p in (_HERE, _ROOT):
         sys.path.insert(0, p)
 
 
+# The HIP runtime of the process must be PyTorch's (libgdn.so binds to
+# whichever libamdhip64.so.7 is loaded first), so torch is imported before any
+# test loads the library.
+import torch  # noqa: E402,F401
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")

@@ -86,7 +86,8 @@ def test_verify_rejects_null_and_misaligned(lib):
     assert verify_call(lib, good(), x=None) == 1
     assert verify_call(lib, good(), o=None) == 1
     assert verify_call(lib, good(), st=FAKE + 4) == 4
-    assert verify_call(lib, good(), cur=FAKE + 8) == 4
+    assert verify_call(lib, good(), cur=FAKE + 2) == 4
+    assert verify_call(lib, good(), g=FAKE + 4) == 4
     f = lib.gdn_verify
     f.argtypes = [ctypes.c_void_p] * 13
     assert f(None, *([FAKE] * 12)) == 1
