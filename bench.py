@@ -58,6 +58,21 @@ def copy_probe(torch):
                       "copies": 3}), flush=True)
 
 
+def counted_traffic(key):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    (calibrated on a plain copy) for the kernel source they were taken on;
+    None when that source has changed since."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f)[key]
+        with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes_per_launch"] if sha == rec["sha256_16"] else None
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -407,7 +422,8 @@ def main():
                    "state": "fp32", "keep": "U{0,1,2} per cycle"},
         "roofline": {"bound": "hbm", "kernel": "gdn::recurrent_kernel<128,128,bf16> (verify)",
                      "achieved": h["verify_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": h["verify_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                     "frac": h["verify_gbs"] / HBM_PEAK_GBS,
+                     "traffic": counted_traffic("recurrent_kernel_verify_b8_t2_l30"),
                      "algorithmic_bytes_per_launch": vb,
                      "avg_launch_ms": h["verify_ms"]},
         "cycle_gbs": h["cycle_gbs"],
