@@ -341,6 +341,73 @@ def conv_step(torch, gb, W, args):
     return dict(tokens=sh.T, ms_per_call=ms, gbs=byts / (ms / 1e3) / 1e9)
 
 
+def prefill(torch, gb, W, args):
+    """Chunked prefill of 4,096-token prompts in 1,024-token calls (chunk 64),
+    32 value / 16 qk heads, d = 128, bf16 inputs and outputs, fp32 state;
+    10 prompt buffers (640 MiB of y) rotated so inputs come from HBM."""
+    sh = W.PREFILL
+    d = gb.make_dims(1, 1, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=1, act="bf16", out="bf16")
+    nb, calls = 10, W.PREFILL_TOKENS // sh.T
+    C = sh.C
+    bf = torch.bfloat16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5005)
+    ys, gs, bs = [], [], []
+    for _ in range(nb):
+        y = torch.randn((calls, 1, 1, sh.T, C), generator=gen, device="cuda")
+        qk = y[..., :2 * sh.HK * sh.DK].reshape(calls, 1, 1, sh.T, 2 * sh.HK, sh.DK)
+        qk /= qk.norm(dim=-1, keepdim=True)
+        ys.append(y.to(bf))
+        gs.append((-torch.nn.functional.softplus(torch.randn((calls, 1, 1, sh.T, sh.HV),
+                                                             generator=gen, device="cuda"))).to(bf))
+        bs.append(torch.sigmoid(torch.randn((calls, 1, 1, sh.T, sh.HV), generator=gen,
+                                            device="cuda")).to(bf))
+    st = torch.zeros((1, 1, 1, sh.HV, sh.DK, sh.DV), device="cuda")
+    o = torch.empty((1, 1, sh.T, sh.HV, sh.DV), device="cuda", dtype=bf)
+    ws = torch.empty(gb.gdn_workspace_size(d), dtype=torch.uint8, device="cuda")
+
+    def prompt(i):
+        st.zero_()
+        for c in range(calls):
+            gb.gdn_prefill_chunked(d, ys[i][c], gs[i][c], bs[i][c], st, None, o, 64, ws)
+
+    for i in range(2):
+        prompt(i)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    reps = 20
+    marks = []
+    start = tm.ev()
+    for r in range(reps):
+        i = r % nb
+        st.zero_()
+        for c in range(calls):
+            e0 = tm.ev()
+            gb.gdn_prefill_chunked(d, ys[i][c], gs[i][c], bs[i][c], st, None, o, 64, ws)
+            e1 = tm.ev()
+            marks.append((e0, e1))
+    end = tm.ev()
+    torch.cuda.synchronize()
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in marks]))
+    total_ms = start.elapsed_time(end)
+    Cc, dd = 64, sh.DK
+    flop_tok_head = 6 * dd * dd + 5 * Cc * dd + Cc * Cc / 3.0
+    flops = flop_tok_head * sh.T * sh.HV
+    byts = sh.T * C * 2 + 2 * sh.T * sh.HV * 2 + 2 * sh.HV * sh.DK * sh.DV * 4 \
+        + sh.T * sh.HV * sh.DV * 2
+    ai = flops / byts
+    attainable = min(2500.0, ai * HBM_PEAK_GBS / 1e3)   # TFLOP/s
+    tflops = flops / (call_ms / 1e3) / 1e12
+    del ys, gs, bs
+    torch.cuda.empty_cache()
+    return dict(call_ms=call_ms, tokens_per_s=calls * sh.T * reps / (total_ms / 1e3),
+                flop_per_call=flops, bytes_per_call=byts, flop_per_byte=ai,
+                achieved_tflops=tflops, mfma_peak_tflops=2500.0,
+                frac_of_mfma_peak=tflops / 2500.0, attainable_tflops=attainable,
+                frac_of_attainable=tflops / attainable,
+                hbm_gbs=byts / (call_ms / 1e3) / 1e9, workspace_bytes=ws.numel())
+
+
 def cpu_baseline(W, budget_s=12.0):
     """The oracle as it stands (single-threaded C, float64) on a bounded
     sample of the headline workload: whole verify + commit layer-cycles of
@@ -393,7 +460,8 @@ def main():
     extra = {}
     if not args.only_headline:
         for name, fn in (("per_layer_graph_b8_t2", per_layer_graph), ("solo_b1_t3_l30", solo),
-                         ("rewind_b8_t4", rewind), ("conv_step_t1024", conv_step)):
+                         ("rewind_b8_t4", rewind), ("conv_step_t1024", conv_step),
+                         ("prefill_b1_4096_in_1024_calls", prefill)):
             log("bench: %s" % name)
             extra[name] = fn(torch, gb, W, args)
             log("bench: %s -> %s" % (name, json.dumps(extra[name])))

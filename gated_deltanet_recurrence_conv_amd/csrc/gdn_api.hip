@@ -209,6 +209,8 @@ gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* y, const void* g, 
     if (chunk != 64) return GDN_E_SHAPE;
     st = check_ptrs({y, g, beta, state, o}, {workspace}, {cur, err});
     if (st != GDN_OK) return st;
+    if (!gdn::prefill_supported(d->DK, d->DV, d->act)) return GDN_E_UNSUPPORTED;
+    if (st != GDN_OK) return st;
     const size_t need = gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, chunk);
     if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
     gdn::PrefillParams p{};

@@ -92,6 +92,7 @@ struct PrefillParams {
     float scale, l2_eps;
     uint32_t flags;
 };
+bool prefill_supported(int DK, int DV, int act);
 size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int chunk);
 hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s);
 

@@ -1,0 +1,204 @@
+"""GPU parity of the chunked prefill (WY/UT form on MFMA) and the standalone
+conv step against the token-sequential CPU oracle, through the C ABI.
+
+"perf(qwen): full-context MTP draft prefill and replay-free rewind"
+(Measurements): 1,024-token layer-major prefill calls; "MTP inference:
+review and commit structure" (Verification and limits): the chunk recurrence
+differs from the sequential one only in rounding.  Tolerance: normwise per
+(layer, row, head) block <= 2e-3 (bf16 inputs, fp32 state and outputs).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gated_deltanet_recurrence_conv_amd import workloads as W
+from gpu_util import act_dtype, dev, dims_pair, host, out_err, state_err, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+def B():
+    from gated_deltanet_recurrence_conv_amd import binding
+    return binding
+
+
+def gpu_prefill(sh, inp, T=None, state=None, out="f32", calls=None):
+    """Run the prefill over inp's tokens, split into `calls` (list of lengths)."""
+    torch = torch_mod()
+    T = sh.T if T is None else T
+    calls = [T] if calls is None else calls
+    A = act_dtype(sh.act)
+    st = dev(inp["state"] if state is None else state, torch.float32)
+    cur = dev(inp["cur"], torch.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    outs = []
+    t0 = 0
+    for n in calls:
+        d, _ = dims_pair(sh, T=n, out=out)
+        y = dev(np.ascontiguousarray(inp["y"][:, :, t0:t0 + n]), A)
+        g = dev(np.ascontiguousarray(inp["g"][:, :, t0:t0 + n]), A)
+        be = dev(np.ascontiguousarray(inp["beta"][:, :, t0:t0 + n]), A)
+        o = torch.full((sh.L, sh.B, n, sh.HV, sh.DV), float("nan"), device="cuda",
+                       dtype=act_dtype(out))
+        ws = torch.empty(max(B().gdn_workspace_size(d), 1), dtype=torch.uint8, device="cuda")
+        B().gdn_prefill_chunked(d, y, g, be, st, cur, o, 64, ws, err)
+        outs.append(o)
+        t0 += n
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    return host(st), np.concatenate([host(o) for o in outs], axis=2)
+
+
+def oracle_prefill(sh, inp, T=None, state=None):
+    T = sh.T if T is None else T
+    _, od = dims_pair(sh, T=T)
+    st0 = inp["state"] if state is None else state
+    return oracle.prefill(od, inp["y"][:, :, :T], inp["g"][:, :, :T], inp["beta"][:, :, :T], st0,
+                          inp["cur"])
+
+
+@pytest.mark.parametrize("T,DK,DV,HV,HK", [(150, 64, 64, 4, 2), (1, 128, 128, 2, 1),
+                                           (13, 32, 16, 2, 2), (64, 128, 32, 2, 1),
+                                           (65, 64, 128, 4, 1), (1000, 128, 128, 2, 1)])
+def test_prefill_shapes_ragged(T, DK, DV, HV, HK):
+    sh = W.Shape("pf", L=1, B=2, T=T, HV=HV, HK=HK, DK=DK, DV=DV, S=2)
+    inp = W.prefill_inputs(sh, seed=3000 + T + DK + DV)
+    inp["state"] = W.random_state(sh, seed=3001)
+    inp["cur"] = np.array([[1, 0]], np.int32)
+    st_g, o_g = gpu_prefill(sh, inp)
+    st_r, o_r, err = oracle_prefill(sh, inp)
+    assert err == 0
+    assert out_err(o_g, o_r) <= 2e-3
+    assert state_err(st_g, st_r) <= 2e-3
+    # the slot that is not cur is untouched
+    assert np.array_equal(st_g[0, 0, 0], inp["state"][0, 0, 0])
+    assert np.array_equal(st_g[0, 1, 1], inp["state"][0, 1, 1])
+
+
+def test_prefill_qwen_4096_tokens_in_1024_calls():
+    """B=1, 4,096-token prompt in 1,024-token calls, chunk 64, 32 value heads,
+    16 qk heads, d = 128, bf16 inputs, fp32 state from zero; every output and
+    the state after each call against the token-sequential oracle."""
+    sh = W.PREFILL
+    inp = W.prefill_inputs(sh, seed=3100, tokens=W.PREFILL_TOKENS)
+    _, od = dims_pair(sh, T=W.PREFILL_TOKENS)
+    st_r, o_r, err = oracle.prefill(od, inp["y"], inp["g"], inp["beta"], inp["state"], inp["cur"])
+    assert err == 0
+    st_g, o_g = gpu_prefill(sh, inp, T=W.PREFILL_TOKENS, calls=[1024] * 4)
+    e_o, e_s = out_err(o_g, o_r), state_err(st_g, st_r)
+    print("prefill 4096: out err %.3e state err %.3e" % (e_o, e_s))
+    assert e_o <= 2e-3 and e_s <= 2e-3
+    # state after the first call too
+    _, od1 = dims_pair(sh, T=1024)
+    st1, _, _ = oracle.prefill(od1, inp["y"][:, :, :1024], inp["g"][:, :, :1024],
+                               inp["beta"][:, :, :1024], inp["state"], inp["cur"])
+    st_g1, _ = gpu_prefill(sh, inp, T=1024, calls=[1024])
+    assert state_err(st_g1, st1) <= 2e-3
+
+
+def test_prefill_carried_state_and_split_calls_bit_exact():
+    """A random N(0, 0.1^2) starting state; calls of 64-multiples give the
+    same bits as one call; a ragged split still matches the oracle."""
+    sh = W.PREFILL.with_(HV=4, HK=2)
+    inp = W.prefill_inputs(sh, seed=3200, tokens=640)
+    inp["state"] = W.random_state(sh, seed=3201)
+    st1, o1 = gpu_prefill(sh, inp, T=640, calls=[640])
+    st2, o2 = gpu_prefill(sh, inp, T=640, calls=[256, 64, 320])
+    assert np.array_equal(st1, st2)
+    assert np.array_equal(o1, o2)
+    st3, o3 = gpu_prefill(sh, inp, T=640, calls=[100, 413, 127])
+    st_r, o_r, _ = oracle_prefill(sh, inp, T=640)
+    assert out_err(o3, o_r) <= 2e-3 and state_err(st3, st_r) <= 2e-3
+    assert out_err(o1, o_r) <= 2e-3 and state_err(st1, st_r) <= 2e-3
+
+
+def test_prefill_bf16_output_and_scale():
+    sh = W.Shape("pfo", L=2, B=1, T=200, HV=2, HK=1, DK=128, DV=64, S=1, out="bf16")
+    inp = W.prefill_inputs(sh, seed=3300)
+    inp["state"] = W.random_state(sh, seed=3301)
+    torch = torch_mod()
+    d, od = dims_pair(sh, out="bf16", scale=128 ** -0.5)
+    y, g, be = (dev(inp[k], torch.bfloat16) for k in ("y", "g", "beta"))
+    st = dev(inp["state"], torch.float32)
+    o = torch.empty((sh.L, sh.B, sh.T, sh.HV, sh.DV), device="cuda", dtype=torch.bfloat16)
+    ws = torch.empty(B().gdn_workspace_size(d), dtype=torch.uint8, device="cuda")
+    B().gdn_prefill_chunked(d, y, g, be, st, None, o, 64, ws)
+    torch.cuda.synchronize()
+    st_r, o_r, _ = oracle.prefill(od, inp["y"], inp["g"], inp["beta"], inp["state"])
+    assert state_err(host(st), st_r) <= 2e-3
+    o_g = host(o).astype(np.float64)
+    # bf16 output: the oracle's value rounded to bf16, within one more bf16 unit
+    assert out_err(o_g, W.bf16_round(o_r.astype(np.float32))) <= 2 ** -7
+
+
+def test_verify_window_matches_prefill():
+    """Verify over a T-token window and the chunked prefill over the same
+    tokens reach the same state and outputs (two different algorithms).  The
+    conv is the identity on the current token with SiLU off, so both see the
+    same bf16 q, k, v."""
+    torch = torch_mod()
+    sh = W.REWIND.with_(B=2, S=5, T=4)
+    inp = W.verify_inputs(sh, seed=3400)
+    wid = np.zeros_like(inp["conv_w"])
+    wid[..., 3] = 1.0
+    d, od = dims_pair(sh, flags=2)
+    A = act_dtype(sh.act)
+    x, w, cs = dev(inp["x"], A), dev(wid, A), dev(inp["conv_state"], A)
+    g, be = dev(inp["g"], A), dev(inp["beta"], A)
+    st = dev(inp["state"], torch.float32)
+    cur = dev(inp["cur"], torch.int32)
+    o = torch.empty((1, 2, 4, sh.HV, sh.DV), device="cuda")
+    B().gdn_verify(d, x, w, None, cs, g, be, st, cur, o, None)
+    st2 = dev(inp["state"], torch.float32)
+    o2 = torch.empty((1, 2, 4, sh.HV, sh.DV), device="cuda")
+    ws = torch.empty(B().gdn_workspace_size(d), dtype=torch.uint8, device="cuda")
+    B().gdn_prefill_chunked(d, x, g, be, st2, cur, o2, 64, ws)
+    torch.cuda.synchronize()
+    sv = host(st)[:, :, 4]            # verify candidate after 4 tokens (cur = 0, S = 5)
+    sp = host(st2)[:, :, 0]
+    assert state_err(sp, sv) <= 2e-3
+    assert out_err(host(o2), host(o)) <= 2e-3
+    st_r, o_r, _ = oracle.verify(od, inp["x"], wid, None, inp["conv_state"], inp["g"],
+                                 inp["beta"], inp["state"], inp["cur"])
+    assert state_err(sp, st_r[:, :, 4]) <= 2e-3 and out_err(host(o2), o_r) <= 2e-3
+
+
+@pytest.mark.parametrize("T", [1, 7, 1024])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_conv_step_parity(T, out):
+    """The short causal conv over T tokens at the Qwen channel count
+    (2*16*128 + 32*128 = 8192), rows 1 and 6 inactive, cache committed."""
+    torch = torch_mod()
+    sh = W.COHORT.with_(T=T, B=8 if T < 1024 else 2, inactive=(1, 6) if T < 1024 else (1,))
+    inp = W.verify_inputs(sh, seed=3500 + T)
+    d, od = dims_pair(sh, out=out)
+    A = act_dtype(sh.act)
+    x, w, cs = dev(inp["x"], A), dev(inp["conv_w"], A), dev(inp["conv_state"], A)
+    act = dev(inp["active"], torch.uint8)
+    y = torch.full(inp["x"].shape, float("nan"), device="cuda", dtype=act_dtype(out))
+    B().gdn_conv_step(d, x, w, None, cs, y, act, True)
+    torch.cuda.synchronize()
+    y_r, cs_r = oracle.conv_step(od, inp["x"], inp["conv_w"], None, inp["conv_state"],
+                                 y_init=np.full(inp["x"].shape, np.nan), active=inp["active"])
+    assert np.array_equal(host(cs).astype(np.float64), cs_r)
+    yg = host(y).astype(np.float64)
+    a = inp["active"].astype(bool)
+    assert np.all(np.isnan(yg[:, ~a]))
+    if out == "f32":
+        assert np.max(np.abs(yg[:, a] - y_r[:, a])) <= 1e-5 * np.max(np.abs(y_r[:, a]))
+    else:
+        ref = W.bf16_round(y_r[:, a].astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(yg[:, a] - ref) <= np.abs(ref) * 2 ** -7 + 1e-30)
+
+
+def test_prefill_rejects_unsupported_and_small_workspace():
+    torch = torch_mod()
+    sh = W.Shape("pfx", L=1, B=1, T=64, HV=2, HK=1, DK=16, DV=16, S=1)
+    d, _ = dims_pair(sh)
+    z = torch.zeros(64 * sh.C, dtype=torch.bfloat16, device="cuda")
+    st = torch.zeros(2 * 16 * 16, device="cuda")
+    o = torch.zeros(64 * 2 * 16, device="cuda")
+    gg = torch.zeros(64 * 2, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(B().GdnError) as ei:
+        B().gdn_prefill_chunked(d, z, gg, gg, st, None, o, 64, torch.zeros(1 << 20, dtype=torch.uint8, device="cuda"))
+    assert ei.value.status == 5   # d_k = 16 is not supported by the chunked kernels
