@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="run one secondary measurement (per_layer_graph, solo, rewind, conv_step, "
+                         "prefill) and print its JSON instead of the headline line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (used to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters)")
@@ -454,6 +457,11 @@ def main():
         copy_probe(torch)
         return
     log("bench: %s on %s" % (gb.gdn_version(), torch.cuda.get_device_name(0)))
+    sections = {"per_layer_graph": per_layer_graph, "solo": solo, "rewind": rewind,
+                "conv_step": conv_step, "prefill": prefill}
+    if args.only:
+        print(json.dumps({args.only: sections[args.only](torch, gb, W, args)}), flush=True)
+        return
     log("bench: headline B8/T2 cohort x %d layers, %d steps" % (L_POOL, args.steps))
     h = headline(torch, gb, W, args)
     log("bench: headline %.4f ms/step  verify %.1f GB/s" % (h["ms_per_step"], h["verify_gbs"]))

@@ -103,13 +103,21 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t u)
     return __uint_as_float(static_cast<uint32_t>(u) << 16);
 }
 
-// float -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+typedef __bf16 gdn_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float gdn_f32x2 __attribute__((ext_vector_type(2)));
+
+// float -> bf16 bits, round to nearest, ties to even (gfx950's
+// v_cvt_pk_bf16_f32; NaN stays a quiet NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// Two floats -> packed bf16x2 (a in the low half), one instruction.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b)
+{
+    const gdn_f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, gdn_bf16x2));
 }
 
 // Activation element as fp32; ACT is a compile-time dtype so that loads are

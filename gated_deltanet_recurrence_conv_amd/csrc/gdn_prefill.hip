@@ -35,6 +35,17 @@
 // MFMA fragment layout (16x16x32 bf16, wave64): A (16 x 32): lane l holds row
 // l%16, k = 8*(l/16)..+8; B (32 x 16): lane l holds column l%16, k =
 // 8*(l/16)..+8; C (16 x 16): lane l holds column l%16, rows 4*(l/16)..+4.
+// 16x16x4 fp32: A: lane l holds A[l%16][l/16]; B: B[l/16][l%16]; C as above.
+//
+// Fragments whose contraction index is a token index or whose row/column
+// roles get swapped use a permuted k order inside each 32-wide block: element
+// e of lane group q = l/16 stands for k = 4q + e (e < 4) or 16 + 4q + (e - 4),
+// i.e. the rows of two stacked C tiles.  A fixed permutation of the
+// contraction index does not change a product, and it lets a C-layout result
+// be used as an operand with no data exchange.  Operands that need the
+// transposed orientation (K^T, and V as a B operand over tokens) are made by
+// multiplying the row-major tile by a 0/1 selection matrix on the MFMA, which
+// is exact and lands the data in C layout, instead of 2-byte LDS transposes.
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -54,89 +65,109 @@ __device__ __forceinline__ f32x4 mfma(const uint4& a, const uint4& b, f32x4 c)
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint2 pack4(uint16_t a, uint16_t b, uint16_t c, uint16_t d)
+__device__ __forceinline__ f32x4 mfma32(float a, float b, f32x4 c)
 {
-    return make_uint2(static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16),
-                      static_cast<uint32_t>(c) | (static_cast<uint32_t>(d) << 16));
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// hi = bf16(x), lo = bf16(x - hi)
-__device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo)
+// hi = bf16(a), lo = bf16(a - hi), two values at a time (packed bf16x2)
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo)
 {
-    hi = f32_to_bf16_bits(x);
-    lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+    hi = f32x2_to_bf16x2(a, b);
+    lo = f32x2_to_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
+// 8 floats -> one bf16x8 fragment
+__device__ __forceinline__ uint4 cvt8(const float* v)
+{
+    return make_uint4(f32x2_to_bf16x2(v[0], v[1]), f32x2_to_bf16x2(v[2], v[3]),
+                      f32x2_to_bf16x2(v[4], v[5]), f32x2_to_bf16x2(v[6], v[7]));
+}
+
+// 8 floats -> hi and lo bf16x8 fragments
+__device__ __forceinline__ void split8(const float* v, uint4& hi, uint4& lo)
+{
+    split2(v[0], v[1], hi.x, lo.x);
+    split2(v[2], v[3], hi.y, lo.y);
+    split2(v[4], v[5], hi.z, lo.z);
+    split2(v[6], v[7], hi.w, lo.w);
 }
 
 // Byte layout of one (layer, row, value head, chunk) record in the workspace.
 template <int DK, int DV>
 struct Rec {
     static constexpr int KS = DK / 32;                           // k-steps over d_k
-    static constexpr size_t WT = 0;                              // W~ A-frags [4][KS][64] x 16 B
+    static constexpr size_t WT = 0;                              // W~ A-frags [4][KS][64] x 16 B (permuted d_k)
     static constexpr size_t UT = WT + 4 * KS * 64 * 16;          // U~ C-frags [4][DV/16][64] x 16 B
-    static constexpr size_t PH = UT + 4 * (DV / 16) * 64 * 16;   // P hi A-frags [4][2][64] x 16 B
+    static constexpr size_t PH = UT + 4 * (DV / 16) * 64 * 16;   // P hi A-frags [4][2][64] x 16 B (permuted tokens)
     static constexpr size_t PL = PH + 4 * 2 * 64 * 16;           // P lo
-    static constexpr size_t KT = PL + 4 * 2 * 64 * 16;           // K^T A-frags [DK/16][2][64] x 16 B
+    static constexpr size_t KT = PL + 4 * 2 * 64 * 16;           // K^T A-frags [DK/16][2][64] x 16 B (permuted tokens)
     static constexpr size_t VEC = KT + (DK / 16) * 2 * 64 * 16;  // qs[64], ks[64], gC
     static constexpr size_t BYTES = VEC + 3 * 64 * 4;
 };
 
-// LDS plan of the prep kernel (bytes).  Region X is reused phase by phase:
-//  phase 1: Ks, Qs rows                       [X, X + 2*64*KP*2)
-//  phase 2: Af (A), Xs (scratch), Tf (T), Pst (P staging)
-//  phase 3: T1h, T1l, T2 over Pst and beyond; Wst (W~ staging) over Af/Xs
-template <int DK, int DV>
-struct PrepLds {
-    static constexpr int KP = DK + 8;
-    static constexpr size_t KST = 0;                                 // K^T [DK][TP] bf16
-    static constexpr size_t VST = KST + static_cast<size_t>(DK) * TP * 2;   // V^T [DV][TP] bf16
-    static constexpr size_t VECS = VST + static_cast<size_t>(DV) * TP * 2;  // G, beta, 1/|q|, 1/|k|
-    static constexpr size_t X = VECS + 4 * CH * 4;
-    // phase 1
-    static constexpr size_t KS_ = X;
-    static constexpr size_t QS_ = X + static_cast<size_t>(CH) * KP * 2;
-    static constexpr size_t P1_END = QS_ + static_cast<size_t>(CH) * KP * 2;
-    // phase 2
-    static constexpr size_t AF = X;                                  // float [64][65]
-    static constexpr size_t XS = AF + CH * (CH + 1) * 4;             // float [3][16][17]
-    static constexpr size_t TF = XS + 3 * 16 * 17 * 4;               // float [64][65]
-    static constexpr size_t PST = TF + CH * (CH + 1) * 4;            // bf16 [2][64][TP]
-    static constexpr size_t P2_END = PST + 2 * CH * TP * 2;
-    // phase 3
-    static constexpr size_t T1H = PST;                               // bf16 [64][TP]
-    static constexpr size_t T1L = T1H + CH * TP * 2;
-    static constexpr size_t T2 = T1L + CH * TP * 2;
-    static constexpr size_t P3_END = T2 + CH * TP * 2;
-    static constexpr size_t WST = X;                                 // bf16 [64][KP]
-    static_assert(WST + static_cast<size_t>(CH) * KP * 2 <= TF, "W~ staging overlaps T");
-    static constexpr size_t END1 = P1_END > P2_END ? P1_END : P2_END;
-    static constexpr size_t BYTES = END1 > P3_END ? END1 : P3_END;
-};
+// 0/1 selection fragment (B operand, 32 x 16): B[k][n] = (k == n + 16 half).
+__device__ __forceinline__ uint4 select_frag(int lane, int half)
+{
+    const int fr = lane & 15, gq = lane >> 4;
+    uint32_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (8 * gq + e == fr + 16 * half) ? 0x3f80u : 0u;   // bf16 1.0
+    return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+}
+
+// Two C tiles (rows 0..15 and 16..31 of a 32-row block, one column per lane)
+// -> one fragment over the permuted 32-wide k order.
+__device__ __forceinline__ uint4 frag_from_c(const f32x4& lo, const f32x4& hi)
+{
+    const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return cvt8(v);
+}
+
+// 16x16 block product on fp32 MFMA, operands in LDS with row pitches XP, YP
+// (floats): acc += X[xr.., xc..] * Y[yr.., yc..].
+template <int XP, int YP>
+__device__ __forceinline__ f32x4 blk_mul(const float* X, int xr, int xc, const float* Y, int yr, int yc,
+                                         f32x4 acc, int fr, int gq)
+{
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        acc = mfma32(X[(xr + fr) * XP + xc + 4 * kk + gq], Y[(yr + 4 * kk + gq) * YP + yc + fr], acc);
+    return acc;
+}
+
+template <int MP>
+__device__ __forceinline__ void blk_store(float* M, int r0, int c0, const f32x4& v, float sgn, int fr, int gq)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) M[(r0 + 4 * gq + j) * MP + c0 + fr] = sgn * v[j];
+}
 
 // ---------------------------------------------------------------------------
-// prep kernel: one workgroup per (chunk, value head, layer*row).
+// prep kernel: one workgroup per (chunk, value head, layer*row).  Wave w owns
+// token tile w (tokens 16w..16w+15 of the chunk): the columns of its K K^T
+// and K Q^T products and the rows of P, U~ and W~.
 template <int DK, int DV>
-__global__ __launch_bounds__(NTHR) void prefill_prep_kernel(PrefillParams p)
+__global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
 {
     using R = Rec<DK, DV>;
-    using S = PrepLds<DK, DV>;
-    constexpr int KP = S::KP;
-    __shared__ __align__(16) char smem[S::BYTES];
-    auto KsT = reinterpret_cast<uint16_t(*)[TP]>(smem + S::KST);
-    auto VsT = reinterpret_cast<uint16_t(*)[TP]>(smem + S::VST);
-    float* Gs = reinterpret_cast<float*>(smem + S::VECS);
-    float* Bs = Gs + CH;
-    float* Inq = Bs + CH;
-    float* Ink = Inq + CH;
-    auto Ks = reinterpret_cast<uint16_t(*)[KP]>(smem + S::KS_);
-    auto Qs = reinterpret_cast<uint16_t(*)[KP]>(smem + S::QS_);
-    auto Af = reinterpret_cast<float(*)[CH + 1]>(smem + S::AF);
-    auto Xs = reinterpret_cast<float(*)[16][17]>(smem + S::XS);
-    auto Tf = reinterpret_cast<float(*)[CH + 1]>(smem + S::TF);
-    auto Pst = reinterpret_cast<uint16_t(*)[CH][TP]>(smem + S::PST);
-    auto T1h = reinterpret_cast<uint16_t(*)[TP]>(smem + S::T1H);
-    auto T1l = reinterpret_cast<uint16_t(*)[TP]>(smem + S::T1L);
-    auto T2 = reinterpret_cast<uint16_t(*)[TP]>(smem + S::T2);
-    auto Wst = reinterpret_cast<uint16_t(*)[KP]>(smem + S::WST);
+    constexpr int KS = DK / 32;
+    constexpr int KP = DK + 8;   // bf16 row pitch of K rows
+    constexpr int VP = DV + 8;   // bf16 row pitch of V rows
+    constexpr int FP = CH + 4;   // fp32 row pitch of A and T (16-byte rows)
+    // region 1: K and V rows (bf16) while loading; A and T (fp32) afterwards
+    constexpr size_t R1A = static_cast<size_t>(CH) * KP * 2 + static_cast<size_t>(CH) * VP * 2;
+    constexpr size_t R1B = 2 * static_cast<size_t>(CH) * FP * 4;
+    __shared__ __align__(16) char r1[R1A > R1B ? R1A : R1B];
+    __shared__ __align__(16) uint4 KTf[DK / 16][2][64];   // K^T A-frags (permuted tokens)
+    __shared__ __align__(16) uint4 Vf[DV / 16][2][64];    // V B-frags (permuted tokens)
+    constexpr int SP = 17;       // fp32 row pitch of the inverse scratch
+    __shared__ float Scr[4][2][16][SP];                   // per-wave scratch for the inverse
+    __shared__ float Gs[CH], Bs[CH], Ink[CH];
+    auto Ks = reinterpret_cast<uint16_t(*)[KP]>(r1);
+    auto Vs = reinterpret_cast<uint16_t(*)[VP]>(r1 + static_cast<size_t>(CH) * KP * 2);
+    float* Af = reinterpret_cast<float*>(r1);
+    float* Tf = reinterpret_cast<float*>(r1) + CH * FP;
 
     const int c = blockIdx.x;
     const int hv = blockIdx.y;
@@ -148,247 +179,273 @@ __global__ __launch_bounds__(NTHR) void prefill_prep_kernel(PrefillParams p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    const int fr = lane & 15;         // fragment row / column
-    const int fk = (lane >> 4) * 8;   // fragment k offset (A, B)
-    const int fq = (lane >> 4) * 4;   // fragment row offset (C)
+    const int fr = lane & 15;          // fragment row / column
+    const int gq = lane >> 4;          // lane group
+    const int fk = gq * 8;             // standard k offset of A/B fragments
+    const int fq = gq * 4;             // row offset of C fragments
     const size_t C = p.C;
     const bool l2 = (p.flags & FLAG_L2) != 0;
     const uint16_t* y = static_cast<const uint16_t*>(p.y);
+    const size_t ybase = static_cast<size_t>(lb) * p.T + t0;   // token row of chunk start
 
-    // ---- phase 1: load q, k (qk head m) and v (value head hv) rows ----
+    // ---- every global load first; rows past the chunk re-read its last row ----
+    const int lr = tid >> 2;     // token row of this thread's K / V vectors
+    const int sub = tid & 3;
+    constexpr int NKV = DK / 32;                     // 16-byte K vectors per thread
+    constexpr int NVV = (DV / 8 + 3) / 4;            // 16-byte V vectors per thread
+    uint4 kv[NKV], vv[NVV], qf[KS];
     {
-        const int r = tid >> 2;   // 4 threads per token row
-        const int sub = tid & 3;
-        const bool real = r < n;
-        const size_t row = (static_cast<size_t>(lb) * p.T + t0 + (real ? r : 0)) * C;
-        float sq = 0.f, sk = 0.f;
+        const size_t row = (ybase + min(lr, n - 1)) * C;
 #pragma unroll
-        for (int v = sub; v < DK / 8; v += 4) {
-            uint4 qv = make_uint4(0, 0, 0, 0), kv = make_uint4(0, 0, 0, 0);
-            if (real) {
-                qv = *reinterpret_cast<const uint4*>(y + row + static_cast<size_t>(m) * DK + v * 8);
-                kv = *reinterpret_cast<const uint4*>(y + row + static_cast<size_t>(p.HK + m) * DK + v * 8);
-            }
-            *reinterpret_cast<uint4*>(&Qs[r][v * 8]) = qv;
-            *reinterpret_cast<uint4*>(&Ks[r][v * 8]) = kv;
-            const uint32_t kw[4] = {kv.x, kv.y, kv.z, kv.w};
-            const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
+        for (int q = 0; q < NKV; ++q)
+            kv[q] = *reinterpret_cast<const uint4*>(y + row + static_cast<size_t>(p.HK + m) * DK + 8 * (sub + 4 * q));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float k0 = __uint_as_float(kw[e] << 16), k1 = __uint_as_float(kw[e] & 0xffff0000u);
-                const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xffff0000u);
-                sk = fmaf(k0, k0, sk);
-                sk = fmaf(k1, k1, sk);
-                sq = fmaf(q0, q0, sq);
-                sq = fmaf(q1, q1, sq);
-                KsT[v * 8 + 2 * e][r] = static_cast<uint16_t>(kw[e] & 0xffffu);
-                KsT[v * 8 + 2 * e + 1][r] = static_cast<uint16_t>(kw[e] >> 16);
-            }
-        }
+        for (int q = 0; q < NVV; ++q)
+            vv[q] = *reinterpret_cast<const uint4*>(y + row + static_cast<size_t>(2 * p.HK) * DK +
+                                                    static_cast<size_t>(hv) * DV + 8 * min(sub + 4 * q, DV / 8 - 1));
+        const size_t qrow = (ybase + min(16 * w + fr, n - 1)) * C + static_cast<size_t>(m) * DK;
 #pragma unroll
-        for (int v = sub; v < DV / 8; v += 4) {
-            uint4 vv = make_uint4(0, 0, 0, 0);
-            if (real)
-                vv = *reinterpret_cast<const uint4*>(y + row + static_cast<size_t>(2 * p.HK) * DK +
-                                                     static_cast<size_t>(hv) * DV + v * 8);
-            const uint32_t vw[4] = {vv.x, vv.y, vv.z, vv.w};
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const uint4*>(y + qrow + 32 * ks + fk);
+    }
+    const size_t gi = (ybase + min(lane, n - 1)) * p.HV + hv;
+    const float graw = load_act<ACT_BF16>(p.g, gi);
+    const float braw = load_act<ACT_BF16>(p.beta, gi);
+
+    // ---- rows into LDS, norms, gates ----
+    const bool lreal = lr < n;
+    float sk = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                VsT[v * 8 + 2 * e][r] = static_cast<uint16_t>(vw[e] & 0xffffu);
-                VsT[v * 8 + 2 * e + 1][r] = static_cast<uint16_t>(vw[e] >> 16);
-            }
-        }
-        // the 4 threads of one row are consecutive lanes (fixed order)
-        sq += __shfl_xor(sq, 1, 64);
-        sq += __shfl_xor(sq, 2, 64);
-        sk += __shfl_xor(sk, 1, 64);
-        sk += __shfl_xor(sk, 2, 64);
-        if (sub == 0) {
-            Inq[r] = (real && l2) ? 1.0f / sqrtf(sq + p.l2_eps) : 1.0f;
-            Ink[r] = (real && l2) ? 1.0f / sqrtf(sk + p.l2_eps) : 1.0f;
+    for (int q = 0; q < NKV; ++q) {
+        if (!lreal) kv[q] = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(&Ks[lr][8 * (sub + 4 * q)]) = kv[q];
+        const uint32_t kw[4] = {kv[q].x, kv[q].y, kv[q].z, kv[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a0 = __uint_as_float(kw[e] << 16), a1 = __uint_as_float(kw[e] & 0xffff0000u);
+            sk = fmaf(a0, a0, sk);
+            sk = fmaf(a1, a1, sk);
         }
     }
-    // gates and the within-chunk cumulative log decay (wave 0, fixed order)
-    if (w == 0) {
-        const size_t gi = (static_cast<size_t>(lb) * p.T + t0 + min(lane, n - 1)) * p.HV + hv;
-        float gv = load_act<ACT_BF16>(p.g, gi);
-        float bv = load_act<ACT_BF16>(p.beta, gi);
-        if (lane >= n) {
-            gv = 0.f;
-            bv = 0.f;
-        }
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
+    for (int q = 0; q < NVV; ++q) {
+        if (!lreal) vv[q] = make_uint4(0, 0, 0, 0);
+        if (sub + 4 * q < DV / 8) *reinterpret_cast<uint4*>(&Vs[lr][8 * (sub + 4 * q)]) = vv[q];
+    }
+    sk += __shfl_xor(sk, 1, 64);   // the 4 threads of a token row are consecutive lanes
+    sk += __shfl_xor(sk, 2, 64);
+    if (sub == 0) Ink[lr] = (l2 && lreal) ? 1.0f / sqrtf(sk + p.l2_eps) : 1.0f;
+    const int r_me = 16 * w + fr;   // this lane's column token
+    if (r_me >= n)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qf[ks] = make_uint4(0, 0, 0, 0);
+    float sq = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t qw[4] = {qf[ks].x, qf[ks].y, qf[ks].z, qf[ks].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a0 = __uint_as_float(qw[e] << 16), a1 = __uint_as_float(qw[e] & 0xffff0000u);
+            sq = fmaf(a0, a0, sq);
+            sq = fmaf(a1, a1, sq);
+        }
+    }
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    const float inq_me = (l2 && r_me < n) ? 1.0f / sqrtf(sq + p.l2_eps) : 1.0f;
+    if (w == 0) {
+        float gv = lane < n ? graw : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {   // inclusive scan, fixed order
             const float o = __shfl_up(gv, off, 64);
             if (lane >= off) gv += o;
         }
         Gs[lane] = gv;
-        Bs[lane] = bv;
+        Bs[lane] = lane < n ? braw : 0.f;
     }
     __syncthreads();
 
-    // ---- K K^T and Q K^T (64 x 64, K = d_k): wave w owns row tile w ----
-    f32x4 kk[4], qk[4];
+    // ---- K K^T and K Q^T: rows i (all tiles), columns r (tile w) ----
+    f32x4 kk[4], kq[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        kk[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        qk[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < 4; ++a) {
+        kk[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        kq[a] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) {
-        const uint4 ak = *reinterpret_cast<const uint4*>(&Ks[16 * w + fr][32 * ks + fk]);
-        const uint4 aq = *reinterpret_cast<const uint4*>(&Qs[16 * w + fr][32 * ks + fk]);
+    for (int ks = 0; ks < KS; ++ks) {
+        const uint4 bk = *reinterpret_cast<const uint4*>(&Ks[16 * w + fr][32 * ks + fk]);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const uint4 bk = *reinterpret_cast<const uint4*>(&Ks[16 * nt + fr][32 * ks + fk]);
-            kk[nt] = mfma(ak, bk, kk[nt]);
-            qk[nt] = mfma(aq, bk, qk[nt]);
+        for (int a = 0; a < 4; ++a) {
+            const uint4 ak = *reinterpret_cast<const uint4*>(&Ks[16 * a + fr][32 * ks + fk]);
+            kk[a] = mfma(ak, bk, kk[a]);
+            kq[a] = mfma(ak, qf[ks], kq[a]);
         }
     }
-    __syncthreads();   // Ks/Qs are overwritten by phase 2
-
-    // ---- phase 2: A (fp32) and P (split bf16) ----
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * w + fq + j;
-            const int i = 16 * nt + fr;
-            const float e = (i <= r) ? expf(Gs[r] - Gs[i]) : 0.f;
-            Af[r][i] = (i < r) ? Bs[r] * e * kk[nt][j] * Ink[r] * Ink[i] : 0.f;
-            const float pv = (i <= r) ? p.scale * e * qk[nt][j] * Inq[r] * Ink[i] : 0.f;
-            uint16_t hi, lo;
-            split_bf16(pv, hi, lo);
-            Pst[0][r][i] = hi;
-            Pst[1][r][i] = lo;
-        }
-    }
-    // upper blocks of T are zero
-    for (int e = tid; e < CH * CH; e += NTHR) {
-        const int r = e / CH, i = e % CH;
-        if ((i >> 4) > (r >> 4)) Tf[r][i] = 0.f;
-    }
-    __syncthreads();
-
-    char* rec = static_cast<char*>(p.ws) +
-                ((static_cast<size_t>(lb) * p.HV + hv) * NC + c) * R::BYTES;
-    // P fragments: [mt][ks][lane] x 8 bf16 along k, hi and lo planes.
-    for (int f = tid; f < 2 * 4 * 2 * 64; f += NTHR) {
-        const int ln = f & 63, ks = (f >> 6) & 1, mt = (f >> 7) & 3, pl = f >> 9;
-        const uint4 v = *reinterpret_cast<const uint4*>(&Pst[pl][16 * mt + (ln & 15)][32 * ks + (ln >> 4) * 8]);
-        *reinterpret_cast<uint4*>(rec + (pl ? R::PL : R::PH) + ((mt * 2 + ks) * 64 + ln) * 16) = v;
-    }
-    // T = (I + A)^-1: diagonal 16x16 blocks, one thread per (block, column)
-    if (tid < 64) {
-        const int bb = tid >> 4, j = tid & 15, o = 16 * bb;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float s = (r == j) ? 1.f : 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (i < r && i >= j) s = fmaf(-Af[o + r][o + i], x[i], s);
-            x[r] = (r < j) ? 0.f : s;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tf[o + r][o + j] = x[r];
-    }
-    __syncthreads();
-    // off-diagonal blocks by distance d: T_ij = -T_ii * sum_{k=j..i-1} A_ik T_kj
-    for (int d = 1; d < 4; ++d) {
-        const int nblk = 4 - d;
-        for (int e = tid; e < nblk * 256; e += NTHR) {
-            const int bj = e >> 8, bi = bj + d, r = (e >> 4) & 15, cc = e & 15;
-            float s = 0.f;
-            for (int bk = bj; bk < bi; ++bk)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    s = fmaf(Af[16 * bi + r][16 * bk + i], Tf[16 * bk + i][16 * bj + cc], s);
-            Xs[bj][r][cc] = s;
-        }
-        __syncthreads();
-        for (int e = tid; e < nblk * 256; e += NTHR) {
-            const int bj = e >> 8, bi = bj + d, r = (e >> 4) & 15, cc = e & 15;
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s = fmaf(Tf[16 * bi + r][16 * bi + i], Xs[bj][i][cc], s);
-            Tf[16 * bi + r][16 * bj + cc] = -s;
-        }
-        __syncthreads();
-    }
-
-    // ---- phase 3: T1 = T diag(beta) (split), T2 = T diag(beta gamma / |k|) ----
-    for (int e = tid; e < CH * CH; e += NTHR) {
-        const int r = e / CH, i = e % CH;
-        const float t = Tf[r][i];
-        uint16_t hi, lo;
-        split_bf16(t * Bs[i], hi, lo);
-        T1h[r][i] = hi;
-        T1l[r][i] = lo;
-        T2[r][i] = f32_to_bf16_bits(t * Bs[i] * expf(Gs[i]) * Ink[i]);
-    }
-    __syncthreads();
-
-    // U~ = T1 V (64 x DV): wave w owns row tile w; written as C-fragments.
+    // ---- K^T and V in token-permuted fragment order via 0/1 selection products ----
+    char* rec = static_cast<char*>(p.ws) + ((static_cast<size_t>(lb) * p.HV + hv) * NC + c) * R::BYTES;
     {
-        f32x4 acc[DV / 16];
+        const uint4 sel0 = select_frag(lane, 0), sel1 = select_frag(lane, 1);
+        for (int db = w; db < DK / 16; db += 4) {
+            f32x4 d4[4];
 #pragma unroll
-        for (int nt = 0; nt < DV / 16; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int tb = 0; tb < 4; ++tb) {
+                const uint4 a = *reinterpret_cast<const uint4*>(&Ks[16 * tb + fr][32 * (db >> 1) + fk]);
+                d4[tb] = mfma(a, (db & 1) ? sel1 : sel0, f32x4{0.f, 0.f, 0.f, 0.f});
+            }
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const uint4 ah = *reinterpret_cast<const uint4*>(&T1h[16 * w + fr][32 * ks + fk]);
-            const uint4 al = *reinterpret_cast<const uint4*>(&T1l[16 * w + fr][32 * ks + fk]);
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint4 f = frag_from_c(d4[2 * ks], d4[2 * ks + 1]);
+                KTf[db][ks][lane] = f;
+                *reinterpret_cast<uint4*>(rec + R::KT + ((db * 2 + ks) * 64 + lane) * 16) = f;
+            }
+        }
+        for (int nt = w; nt < DV / 16; nt += 4) {
+            f32x4 d4[4];
 #pragma unroll
-            for (int nt = 0; nt < DV / 16; ++nt) {
-                const uint4 bv = *reinterpret_cast<const uint4*>(&VsT[16 * nt + fr][32 * ks + fk]);
-                acc[nt] = mfma(ah, bv, acc[nt]);
-                acc[nt] = mfma(al, bv, acc[nt]);
+            for (int tb = 0; tb < 4; ++tb) {
+                const uint4 a = *reinterpret_cast<const uint4*>(&Vs[16 * tb + fr][32 * (nt >> 1) + fk]);
+                d4[tb] = mfma(a, (nt & 1) ? sel1 : sel0, f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) Vf[nt][ks][lane] = frag_from_c(d4[2 * ks], d4[2 * ks + 1]);
+        }
+    }
+    __syncthreads();   // K and V rows are dead from here on (region 1 becomes A and T)
+
+    // ---- A (fp32, LDS), P = scale lower_incl(E o Q^K^T) (split A-frags), per-token vectors ----
+    {
+        const float g_me = Gs[r_me], b_me = Bs[r_me], ink_me = Ink[r_me];
+        float pv[2][8];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 16 * a + fq + j;
+                const float e = (i <= r_me) ? expf(g_me - Gs[i]) : 0.f;
+                const float ink_i = Ink[i];
+                Af[r_me * FP + i] = (i < r_me) ? b_me * e * kk[a][j] * ink_me * ink_i : 0.f;
+                pv[a >> 1][4 * (a & 1) + j] = (i <= r_me) ? p.scale * e * kq[a][j] * inq_me * ink_i : 0.f;
             }
         }
 #pragma unroll
-        for (int nt = 0; nt < DV / 16; ++nt)
-            *reinterpret_cast<f32x4*>(rec + R::UT + ((w * (DV / 16) + nt) * 64 + lane) * 16) = acc[nt];
-    }
-    // W~ = T2 K (64 x DK), staged row-major in bf16, then written as A-fragments.
-    {
-        f32x4 acc[DK / 16];
-#pragma unroll
-        for (int nt = 0; nt < DK / 16; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const uint4 a2 = *reinterpret_cast<const uint4*>(&T2[16 * w + fr][32 * ks + fk]);
-#pragma unroll
-            for (int nt = 0; nt < DK / 16; ++nt) {
-                const uint4 bk = *reinterpret_cast<const uint4*>(&KsT[16 * nt + fr][32 * ks + fk]);
-                acc[nt] = mfma(a2, bk, acc[nt]);
-            }
+            uint4 h, l;
+            split8(pv[ks], h, l);
+            *reinterpret_cast<uint4*>(rec + R::PH + ((w * 2 + ks) * 64 + lane) * 16) = h;
+            *reinterpret_cast<uint4*>(rec + R::PL + ((w * 2 + ks) * 64 + lane) * 16) = l;
         }
-#pragma unroll
-        for (int nt = 0; nt < DK / 16; ++nt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) Wst[16 * w + fq + j][16 * nt + fr] = f32_to_bf16_bits(acc[nt][j]);
-    }
-    __syncthreads();
-    for (int f = tid; f < 4 * R::KS * 64; f += NTHR) {
-        const int ln = f & 63, ks = (f >> 6) % R::KS, mt = (f >> 6) / R::KS;
-        const uint4 v = *reinterpret_cast<const uint4*>(&Wst[16 * mt + (ln & 15)][32 * ks + (ln >> 4) * 8]);
-        *reinterpret_cast<uint4*>(rec + R::WT + ((mt * R::KS + ks) * 64 + ln) * 16) = v;
-    }
-    // K^T A-fragments (row = d_k index, k = token) for the state update.
-    for (int f = tid; f < (DK / 16) * 2 * 64; f += NTHR) {
-        const int ln = f & 63, ks = (f >> 6) & 1, mt = f >> 7;
-        const uint4 v = *reinterpret_cast<const uint4*>(&KsT[16 * mt + (ln & 15)][32 * ks + (ln >> 4) * 8]);
-        *reinterpret_cast<uint4*>(rec + R::KT + ((mt * 2 + ks) * 64 + ln) * 16) = v;
-    }
-    // per-token vectors
-    if (tid < CH) {
-        const int r = tid;
-        const float gl = Gs[n - 1];
         float* vec = reinterpret_cast<float*>(rec + R::VEC);
-        vec[r] = (r < n) ? p.scale * expf(Gs[r]) * Inq[r] : 0.f;
-        vec[CH + r] = (r < n) ? expf(gl - Gs[r]) * Ink[r] : 0.f;
-        vec[2 * CH + r] = expf(gl);
+        if (gq == 0) vec[r_me] = (r_me < n) ? p.scale * expf(g_me) * inq_me : 0.f;
+        if (w == 0) {
+            const float gl = Gs[n - 1];
+            vec[CH + lane] = (lane < n) ? expf(gl - Gs[lane]) * Ink[lane] : 0.f;
+            vec[2 * CH + lane] = expf(gl);
+        }
+        // upper blocks of T are zero
+        for (int e2 = tid; e2 < CH * CH; e2 += NTHR) {
+            const int rr = e2 >> 6, ii = e2 & 63;
+            if ((ii >> 4) > (rr >> 4)) Tf[rr * FP + ii] = 0.f;
+        }
     }
+    __syncthreads();   // A complete
+
+    // ---- T = (I + A)^-1 on fp32 MFMA, 16x16 blocks by recursive doubling ----
+    {
+        float* S0 = &Scr[w][0][0][0];
+        float* S1 = &Scr[w][1][0][0];
+        // diagonal block w: (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8)
+        const int o = 16 * w;
+        f32x4 x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            x[j] = ((fq + j) == fr ? 1.f : 0.f) - Af[(o + fq + j) * FP + o + fr];
+        blk_store<FP>(Tf, o, o, x, 1.f, fr, gq);
+        f32x4 pw = blk_mul<FP, FP>(Af, o, o, Af, o, o, f32x4{0.f, 0.f, 0.f, 0.f}, fr, gq);   // N^2
+        blk_store<SP>(S0, 0, 0, pw, 1.f, fr, gq);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int step = 0; step < 3; ++step) {
+            float* Pcur = (step & 1) ? S1 : S0;
+            float* Pnext = (step & 1) ? S0 : S1;
+            x = blk_mul<FP, SP>(Tf, o, o, Pcur, 0, 0, x, fr, gq);      // X += X P
+            if (step < 2) pw = blk_mul<SP, SP>(Pcur, 0, 0, Pcur, 0, 0, f32x4{0.f, 0.f, 0.f, 0.f}, fr, gq);
+            __builtin_amdgcn_wave_barrier();
+            blk_store<FP>(Tf, o, o, x, 1.f, fr, gq);
+            if (step < 2) blk_store<SP>(Pnext, 0, 0, pw, 1.f, fr, gq);
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+    __syncthreads();
+    // off-diagonal 16x16 blocks of the two 32x32 halves: T10 = -D1 A10 D0, T32 = -D3 A32 D2
+    if (w == 1 || w == 3) {
+        const int b = 16 * (w - 1);   // column block of the pair
+        float* S0 = &Scr[w][0][0][0];
+        const f32x4 xa = blk_mul<FP, FP>(Af, b + 16, b, Tf, b, b, f32x4{0.f, 0.f, 0.f, 0.f}, fr, gq);
+        blk_store<SP>(S0, 0, 0, xa, 1.f, fr, gq);
+        __builtin_amdgcn_wave_barrier();
+        const f32x4 t = blk_mul<FP, SP>(Tf, b + 16, b + 16, S0, 0, 0, f32x4{0.f, 0.f, 0.f, 0.f}, fr, gq);
+        blk_store<FP>(Tf, b + 16, b, t, -1.f, fr, gq);
+    }
+    __syncthreads();
+    // lower-left 32x32 quadrant: X = A[32:64, 0:32] T[0:32, 0:32], then T21 = -T22 X.
+    // Block (pr, pc) of X lives in Scr[pr][pc].
+    {
+        const int pr = w >> 1, pc = w & 1;   // this wave's 16x16 block of X
+        f32x4 xa = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = pc; kb < 2; ++kb)   // T[0:32,0:32] is block lower triangular
+            xa = blk_mul<FP, FP>(Af, 32 + 16 * pr, 16 * kb, Tf, 16 * kb, 16 * pc, xa, fr, gq);
+        blk_store<SP>(&Scr[pr][pc][0][0], 0, 0, xa, 1.f, fr, gq);
+    }
+    __syncthreads();
+    {
+        const int pr = w >> 1, pc = w & 1;
+        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb <= pr; ++kb)   // T[32:64, 32:64] is block lower triangular
+            t = blk_mul<FP, SP>(Tf, 32 + 16 * pr, 32 + 16 * kb, &Scr[kb][pc][0][0], 0, 0, t, fr, gq);
+        blk_store<FP>(Tf, 32 + 16 * pr, 16 * pc, t, -1.f, fr, gq);
+    }
+    __syncthreads();
+
+    // ---- U~ = T diag(beta) V (split T) and W~^T = K^T (T diag(beta gamma / |k|))^T ----
+    // Both read row r_me of T over the permuted token order.
+    uint4 t1h[2], t1l[2], t2[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&Tf[r_me * FP + 32 * ks + fq]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&Tf[r_me * FP + 32 * ks + 16 + fq]);
+        const float tv[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+        float v1[8], v2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = 32 * ks + (e < 4 ? fq + e : 12 + fq + e);
+            v1[e] = tv[e] * Bs[i];
+            v2[e] = v1[e] * expf(Gs[i]) * Ink[i];
+        }
+        split8(v1, t1h[ks], t1l[ks]);
+        t2[ks] = cvt8(v2);
+    }
+#pragma unroll
+    for (int nt = 0; nt < DV / 16; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint4 bvv = Vf[nt][ks][lane];
+            acc = mfma(t1h[ks], bvv, acc);
+            acc = mfma(t1l[ks], bvv, acc);
+        }
+        *reinterpret_cast<f32x4*>(rec + R::UT + ((w * (DV / 16) + nt) * 64 + lane) * 16) = acc;
+    }
+    f32x4 wt[DK / 16];
+#pragma unroll
+    for (int a = 0; a < DK / 16; ++a) {
+        wt[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) wt[a] = mfma(KTf[a][ks][lane], t2[ks], wt[a]);
+    }
+    // wt[a][j] = W~[r_me][d_k = 16a + fq + j]: the permuted-d_k fragment of block a/2
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        *reinterpret_cast<uint4*>(rec + R::WT + ((w * KS + ks) * 64 + lane) * 16) = frag_from_c(wt[2 * ks], wt[2 * ks + 1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -397,12 +454,12 @@ template <int DK, int DV>
 struct ScanFrags {
     static constexpr int KS = DK / 32;
     static constexpr int MQ = (DK / 16 + 3) / 4;   // H' row tiles per wave
-    uint4 wt[KS];      // W~ rows of this wave's token tile
-    uint4 q[KS];       // raw Q rows of this wave's token tile
-    uint4 ph[2], pl[2];
-    uint4 kt[MQ][2];   // K^T rows of this wave's state tiles
-    f32x4 ut;          // U~ tile
-    f32x4 qs, ks;      // per-row output / update scalings
+    uint4 wt[KS];        // W~ rows of this wave's token tile (permuted d_k)
+    uint4 q[KS];         // raw Q rows of this wave's token tile (standard d_k)
+    uint4 ph[2], pl[2];  // P rows (permuted tokens)
+    uint4 kt[MQ][2];     // K^T rows of this wave's state tiles (permuted tokens)
+    f32x4 ut;            // U~ tile
+    f32x4 qs, ks;        // per-row output / update scalings
     float gC;
 };
 
@@ -423,12 +480,10 @@ __device__ __forceinline__ void scan_load(ScanFrags<DK, DV>& f, const char* rec,
     }
 #pragma unroll
     for (int qq = 0; qq < ScanFrags<DK, DV>::MQ; ++qq) {
-        const int mt = w + 4 * qq;
-        if (mt < DK / 16) {
+        const int mt = min(w + 4 * qq, DK / 16 - 1);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                f.kt[qq][ks] = *reinterpret_cast<const uint4*>(rec + R::KT + ((mt * 2 + ks) * 64 + lane) * 16);
-        }
+        for (int ks = 0; ks < 2; ++ks)
+            f.kt[qq][ks] = *reinterpret_cast<const uint4*>(rec + R::KT + ((mt * 2 + ks) * 64 + lane) * 16);
     }
     f.ut = *reinterpret_cast<const f32x4*>(rec + R::UT + ((w * (DV / 16) + cs) * 64 + lane) * 16);
     const float* vec = reinterpret_cast<const float*>(rec + R::VEC);
@@ -438,7 +493,112 @@ __device__ __forceinline__ void scan_load(ScanFrags<DK, DV>& f, const char* rec,
     f.gC = vec[2 * CH];
 }
 
-template <int DK, int DV>
+// A permuted-k B fragment from a [col][k] bf16 row: k = kb + 4q..+4 and kb + 16 + 4q..+4.
+__device__ __forceinline__ uint4 perm_b(const uint16_t* rowp, int kb, int gq)
+{
+    const uint2 a = *reinterpret_cast<const uint2*>(rowp + kb + 4 * gq);
+    const uint2 b = *reinterpret_cast<const uint2*>(rowp + kb + 16 + 4 * gq);
+    return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+template <int DK>
+struct ScanShared {
+    uint16_t (*HTh)[16][DK + 8];
+    uint16_t (*HTl)[16][DK + 8];
+    uint16_t (*UTh)[TP];
+    uint16_t (*UTl)[TP];
+    uint16_t (*STh)[TP];
+    uint16_t (*STl)[TP];
+};
+
+// One chunk of the scan for one wave: U, then O and H'.  FULL: all 64
+// tokens of the chunk exist (no bounds test on the output stores).
+template <int DK, int DV, int OUT, bool FULL>
+__device__ __forceinline__ void scan_chunk(const PrefillParams& p, const ScanFrags<DK, DV>& cur,
+                                           f32x4 (&h)[ScanFrags<DK, DV>::MQ], const ScanShared<DK>& sm,
+                                           int c, int hv, int lb, int col, int w, int lane)
+{
+    using F = ScanFrags<DK, DV>;
+    const int pb = c & 1;
+    const int fr = lane & 15, gq = lane >> 4, fk = gq * 8, fq = gq * 4;
+    // W~ H (permuted d_k) and Q H (standard d_k, hi and lo) on the state at the chunk start
+    f32x4 wh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f}, ql = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < F::KS; ++ks) {
+        const uint4 hp = perm_b(&sm.HTh[pb][fr][0], 32 * ks, gq);
+        const uint4 hb = *reinterpret_cast<const uint4*>(&sm.HTh[pb][fr][32 * ks + fk]);
+        const uint4 hl = *reinterpret_cast<const uint4*>(&sm.HTl[pb][fr][32 * ks + fk]);
+        wh = mfma(cur.wt[ks], hp, wh);
+        qh = mfma(cur.q[ks], hb, qh);
+        ql = mfma(cur.q[ks], hl, ql);
+    }
+    // U = U~ - W~ H; S = diag(s) U; both to LDS, split, transposed
+    float u[4], sv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        u[j] = cur.ut[j] - wh[j];
+        sv[j] = cur.ks[j] * u[j];
+    }
+    uint32_t uh0, ul0, uh1, ul1, sh0, sl0, sh1, sl1;
+    split2(u[0], u[1], uh0, ul0);
+    split2(u[2], u[3], uh1, ul1);
+    split2(sv[0], sv[1], sh0, sl0);
+    split2(sv[2], sv[3], sh1, sl1);
+    *reinterpret_cast<uint2*>(&sm.UTh[fr][16 * w + fq]) = make_uint2(uh0, uh1);
+    *reinterpret_cast<uint2*>(&sm.UTl[fr][16 * w + fq]) = make_uint2(ul0, ul1);
+    *reinterpret_cast<uint2*>(&sm.STh[fr][16 * w + fq]) = make_uint2(sh0, sh1);
+    *reinterpret_cast<uint2*>(&sm.STl[fr][16 * w + fq]) = make_uint2(sl0, sl1);
+    __syncthreads();
+
+    // O = diag(qs) Q H + P U and H' = gC H + K^T S (P, K^T, U, S over the
+    // permuted token order), as independent MFMA chains.
+    f32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = cur.qs[j] * (qh[j] + ql[j]);
+    f32x4 acc[F::MQ];
+#pragma unroll
+    for (int qq = 0; qq < F::MQ; ++qq)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[qq][j] = cur.gC * h[qq][j];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const uint4 bh = perm_b(&sm.UTh[fr][0], 32 * ks, gq);
+        const uint4 bl = perm_b(&sm.UTl[fr][0], 32 * ks, gq);
+        const uint4 sbh = perm_b(&sm.STh[fr][0], 32 * ks, gq);
+        const uint4 sbl = perm_b(&sm.STl[fr][0], 32 * ks, gq);
+        o = mfma(cur.ph[ks], bh, o);
+#pragma unroll
+        for (int qq = 0; qq < F::MQ; ++qq) acc[qq] = mfma(cur.kt[qq][ks], sbh, acc[qq]);
+        o = mfma(cur.ph[ks], bl, o);
+#pragma unroll
+        for (int qq = 0; qq < F::MQ; ++qq) acc[qq] = mfma(cur.kt[qq][ks], sbl, acc[qq]);
+        o = mfma(cur.pl[ks], bh, o);
+    }
+#pragma unroll
+    for (int qq = 0; qq < F::MQ; ++qq) {
+        const int mt = w + 4 * qq;
+        if (mt < DK / 16) {
+            h[qq] = acc[qq];
+            uint32_t hh0, hl0, hh1, hl1;
+            split2(acc[qq][0], acc[qq][1], hh0, hl0);
+            split2(acc[qq][2], acc[qq][3], hh1, hl1);
+            *reinterpret_cast<uint2*>(&sm.HTh[pb ^ 1][fr][16 * mt + fq]) = make_uint2(hh0, hh1);
+            *reinterpret_cast<uint2*>(&sm.HTl[pb ^ 1][fr][16 * mt + fq]) = make_uint2(hl0, hl1);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = c * CH + 16 * w + fq + j;
+        if (FULL || t < p.T) {
+            const size_t oi = ((static_cast<size_t>(lb) * p.T + t) * p.HV + hv) * DV + col;
+            if constexpr (OUT == ACT_BF16) static_cast<uint16_t*>(p.o)[oi] = f32_to_bf16_bits(o[j]);
+            else static_cast<float*>(p.o)[oi] = o[j];
+        }
+    }
+    __syncthreads();
+}
+
+template <int DK, int DV, int OUT>
 __global__ __launch_bounds__(NTHR) void prefill_scan_kernel(PrefillParams p)
 {
     using R = Rec<DK, DV>;
@@ -460,8 +620,9 @@ __global__ __launch_bounds__(NTHR) void prefill_scan_kernel(PrefillParams p)
     const int lane = tid & 63;
     const int w = tid >> 6;
     const int fr = lane & 15;
-    const int fk = (lane >> 4) * 8;
-    const int fq = (lane >> 4) * 4;
+    const int gq = lane >> 4;
+    const int fk = gq * 8;
+    const int fq = gq * 4;
 
     const int slot = p.cur ? p.cur[lb] : 0;
     if (slot < 0 || slot >= p.S) {
@@ -479,11 +640,11 @@ __global__ __launch_bounds__(NTHR) void prefill_scan_kernel(PrefillParams p)
         if (mt < DK / 16) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) h[qq][j] = st[(16 * mt + fq + j) * DV + col];
-            uint16_t hi[4], lo[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) split_bf16(h[qq][j], hi[j], lo[j]);
-            *reinterpret_cast<uint2*>(&HTh[0][fr][16 * mt + fq]) = pack4(hi[0], hi[1], hi[2], hi[3]);
-            *reinterpret_cast<uint2*>(&HTl[0][fr][16 * mt + fq]) = pack4(lo[0], lo[1], lo[2], lo[3]);
+            uint32_t hh0, hl0, hh1, hl1;
+            split2(h[qq][0], h[qq][1], hh0, hl0);
+            split2(h[qq][2], h[qq][3], hh1, hl1);
+            *reinterpret_cast<uint2*>(&HTh[0][fr][16 * mt + fq]) = make_uint2(hh0, hh1);
+            *reinterpret_cast<uint2*>(&HTl[0][fr][16 * mt + fq]) = make_uint2(hl0, hl1);
         }
     }
     __syncthreads();
@@ -495,89 +656,25 @@ __global__ __launch_bounds__(NTHR) void prefill_scan_kernel(PrefillParams p)
         return y + (static_cast<size_t>(lb) * p.T + t) * p.C + static_cast<size_t>(m) * DK + fk;
     };
 
-    F cur;
-    scan_load<DK, DV>(cur, recs, qrow(0), w, lane, cs);
-    for (int c = 0; c < NC; ++c) {
-        const int pb = c & 1;
-        F nxt;
-        if (c + 1 < NC) scan_load<DK, DV>(nxt, recs + static_cast<size_t>(c + 1) * R::BYTES, qrow(c + 1), w, lane, cs);
-
-        // U = U~ - W~ H (this wave's 16 tokens x 16 columns)
-        f32x4 wh = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < R::KS; ++ks) {
-            const uint4 hb = *reinterpret_cast<const uint4*>(&HTh[pb][fr][32 * ks + fk]);
-            wh = mfma(cur.wt[ks], hb, wh);
-        }
-        f32x4 u;
-        uint16_t uh[4], ul[4], sh[4], sl[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            u[j] = cur.ut[j] - wh[j];
-            split_bf16(u[j], uh[j], ul[j]);
-            split_bf16(cur.ks[j] * u[j], sh[j], sl[j]);
-        }
-        *reinterpret_cast<uint2*>(&UTh[fr][16 * w + fq]) = pack4(uh[0], uh[1], uh[2], uh[3]);
-        *reinterpret_cast<uint2*>(&UTl[fr][16 * w + fq]) = pack4(ul[0], ul[1], ul[2], ul[3]);
-        *reinterpret_cast<uint2*>(&STh[fr][16 * w + fq]) = pack4(sh[0], sh[1], sh[2], sh[3]);
-        *reinterpret_cast<uint2*>(&STl[fr][16 * w + fq]) = pack4(sl[0], sl[1], sl[2], sl[3]);
-        __syncthreads();
-
-        // O = diag(qs) Q H + P U
-        f32x4 qh = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < R::KS; ++ks) {
-            const uint4 hb = *reinterpret_cast<const uint4*>(&HTh[pb][fr][32 * ks + fk]);
-            const uint4 lb_ = *reinterpret_cast<const uint4*>(&HTl[pb][fr][32 * ks + fk]);
-            qh = mfma(cur.q[ks], hb, qh);
-            qh = mfma(cur.q[ks], lb_, qh);
-        }
-        f32x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = cur.qs[j] * qh[j];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const uint4 bh = *reinterpret_cast<const uint4*>(&UTh[fr][32 * ks + fk]);
-            const uint4 bl = *reinterpret_cast<const uint4*>(&UTl[fr][32 * ks + fk]);
-            o = mfma(cur.ph[ks], bh, o);
-            o = mfma(cur.ph[ks], bl, o);
-            o = mfma(cur.pl[ks], bh, o);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = c * CH + 16 * w + fq + j;
-            if (t < p.T) {
-                const size_t oi = ((static_cast<size_t>(lb) * p.T + t) * p.HV + hv) * DV + col;
-                if (p.out == ACT_BF16) static_cast<uint16_t*>(p.o)[oi] = f32_to_bf16_bits(o[j]);
-                else static_cast<float*>(p.o)[oi] = o[j];
-            }
-        }
-
-        // H' = gC H + K^T (diag(s) U) for this wave's state tiles
-#pragma unroll
-        for (int qq = 0; qq < F::MQ; ++qq) {
-            const int mt = w + 4 * qq;
-            if (mt < DK / 16) {
-                f32x4 acc;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[j] = cur.gC * h[qq][j];
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const uint4 bh = *reinterpret_cast<const uint4*>(&STh[fr][32 * ks + fk]);
-                    const uint4 bl = *reinterpret_cast<const uint4*>(&STl[fr][32 * ks + fk]);
-                    acc = mfma(cur.kt[qq][ks], bh, acc);
-                    acc = mfma(cur.kt[qq][ks], bl, acc);
-                }
-                h[qq] = acc;
-                uint16_t hi[4], lo[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) split_bf16(acc[j], hi[j], lo[j]);
-                *reinterpret_cast<uint2*>(&HTh[pb ^ 1][fr][16 * mt + fq]) = pack4(hi[0], hi[1], hi[2], hi[3]);
-                *reinterpret_cast<uint2*>(&HTl[pb ^ 1][fr][16 * mt + fq]) = pack4(lo[0], lo[1], lo[2], lo[3]);
-            }
-        }
-        __syncthreads();
-        if (c + 1 < NC) cur = nxt;
+    ScanShared<DK> sm{HTh, HTl, UTh, UTl, STh, STl};
+    // Ping-pong fragment sets; every chunk but the last is full, so its
+    // output stores carry no branch and the next chunk's prefetch can be
+    // waited for without waiting on them.
+    F fa, fb;
+    scan_load<DK, DV>(fa, recs, qrow(0), w, lane, cs);
+    int c = 0;
+    for (; c + 2 < NC; c += 2) {
+        scan_load<DK, DV>(fb, recs + static_cast<size_t>(c + 1) * R::BYTES, qrow(c + 1), w, lane, cs);
+        scan_chunk<DK, DV, OUT, true>(p, fa, h, sm, c, hv, lb, col, w, lane);
+        scan_load<DK, DV>(fa, recs + static_cast<size_t>(c + 2) * R::BYTES, qrow(c + 2), w, lane, cs);
+        scan_chunk<DK, DV, OUT, true>(p, fb, h, sm, c + 1, hv, lb, col, w, lane);
+    }
+    if (c + 1 < NC) {
+        scan_load<DK, DV>(fb, recs + static_cast<size_t>(c + 1) * R::BYTES, qrow(c + 1), w, lane, cs);
+        scan_chunk<DK, DV, OUT, true>(p, fa, h, sm, c, hv, lb, col, w, lane);
+        scan_chunk<DK, DV, OUT, false>(p, fb, h, sm, c + 1, hv, lb, col, w, lane);
+    } else {
+        scan_chunk<DK, DV, OUT, false>(p, fa, h, sm, c, hv, lb, col, w, lane);
     }
 #pragma unroll
     for (int qq = 0; qq < F::MQ; ++qq) {
@@ -600,8 +697,12 @@ hipError_t launch_pf(const PrefillParams& p, hipStream_t s)
                        dim3(NTHR), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((prefill_scan_kernel<DK, DV>), dim3(DV / 16, p.HV, static_cast<unsigned>(rows)),
-                       dim3(NTHR), 0, s, p);
+    if (p.out == ACT_BF16)
+        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16>),
+                           dim3(DV / 16, p.HV, static_cast<unsigned>(rows)), dim3(NTHR), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32>),
+                           dim3(DV / 16, p.HV, static_cast<unsigned>(rows)), dim3(NTHR), 0, s, p);
     return hipGetLastError();
 }
 
