@@ -27,10 +27,11 @@
 //       on the carried state -- norms, G, K K^T, Q K^T, the UT inverse, U~,
 //       W~ -- written as one record per (row, head, chunk) in MFMA fragment
 //       order, so the scan reads it with 16-byte coalesced loads.
-//  scan (grid d_v/16 x value heads x rows): the sequential part.  Each
+//  scan (one workgroup per 16 columns of a head and row): the sequential part.  Each
 //       workgroup owns 16 columns of one head's state (the d_v columns are
-//       independent recurrences) in VGPRs and walks the chunks: U, then O and
-//       H', prefetching the next chunk's fragments while it computes.
+//       independent recurrences): one wave runs the recurrence with the state
+//       in VGPRs, a second wave computes the outputs; both prefetch the next
+//       chunk's fragments while they compute.
 //
 // MFMA fragment layout (16x16x32 bf16, wave64): A (16 x 32): lane l holds row
 // l%16, k = 8*(l/16)..+8; B (32 x 16): lane l holds column l%16, k =
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
     __shared__ __align__(16) uint4 Vf[DV / 16][2][64];    // V B-frags (permuted tokens)
     constexpr int SP = 17;       // fp32 row pitch of the inverse scratch
     __shared__ float Scr[4][2][16][SP];                   // per-wave scratch for the inverse
-    __shared__ float Gs[CH], Bs[CH], Ink[CH];
+    __shared__ float Gs[CH], Bs[CH], Ink[CH];   // Gs: cumulative log2 decay
     auto Ks = reinterpret_cast<uint16_t(*)[KP]>(r1);
     auto Vs = reinterpret_cast<uint16_t(*)[VP]>(r1 + static_cast<size_t>(CH) * KP * 2);
     float* Af = reinterpret_cast<float*>(r1);
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
             const float o = __shfl_up(gv, off, 64);
             if (lane >= off) gv += o;
         }
-        Gs[lane] = gv;
+        Gs[lane] = gv * 1.4426950408889634f;   // log2(e): decays below are exp2 of differences
         Bs[lane] = lane < n ? braw : 0.f;
     }
     __syncthreads();
@@ -303,7 +304,11 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
             f32x4 d4[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-                const uint4 a = *reinterpret_cast<const uint4*>(&Vs[16 * tb + fr][32 * (nt >> 1) + fk]);
+                // with d_v = 16 the upper half of the 32-wide k block is the row
+                // pad (never written): feed zeros, not 0 x garbage
+                const uint4 a = (32 * (nt >> 1) + fk < DV)
+                                    ? *reinterpret_cast<const uint4*>(&Vs[16 * tb + fr][32 * (nt >> 1) + fk])
+                                    : make_uint4(0, 0, 0, 0);
                 d4[tb] = mfma(a, (nt & 1) ? sel1 : sel0, f32x4{0.f, 0.f, 0.f, 0.f});
             }
 #pragma unroll
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int i = 16 * a + fq + j;
-                const float e = (i <= r_me) ? expf(g_me - Gs[i]) : 0.f;
+                const float e = (i <= r_me) ? exp2f(g_me - Gs[i]) : 0.f;
                 const float ink_i = Ink[i];
                 Af[r_me * FP + i] = (i < r_me) ? b_me * e * kk[a][j] * ink_me * ink_i : 0.f;
                 pv[a >> 1][4 * (a & 1) + j] = (i <= r_me) ? p.scale * e * kq[a][j] * inq_me * ink_i : 0.f;
@@ -335,11 +340,11 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
             *reinterpret_cast<uint4*>(rec + R::PL + ((w * 2 + ks) * 64 + lane) * 16) = l;
         }
         float* vec = reinterpret_cast<float*>(rec + R::VEC);
-        if (gq == 0) vec[r_me] = (r_me < n) ? p.scale * expf(g_me) * inq_me : 0.f;
+        if (gq == 0) vec[r_me] = (r_me < n) ? p.scale * exp2f(g_me) * inq_me : 0.f;
         if (w == 0) {
             const float gl = Gs[n - 1];
-            vec[CH + lane] = (lane < n) ? expf(gl - Gs[lane]) * Ink[lane] : 0.f;
-            vec[2 * CH + lane] = expf(gl);
+            vec[CH + lane] = (lane < n) ? exp2f(gl - Gs[lane]) * Ink[lane] : 0.f;
+            vec[2 * CH + lane] = exp2f(gl);
         }
         // upper blocks of T are zero
         for (int e2 = tid; e2 < CH * CH; e2 += NTHR) {
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
         for (int e = 0; e < 8; ++e) {
             const int i = 32 * ks + (e < 4 ? fq + e : 12 + fq + e);
             v1[e] = tv[e] * Bs[i];
-            v2[e] = v1[e] * expf(Gs[i]) * Ink[i];
+            v2[e] = v1[e] * exp2f(Gs[i]) * Ink[i];
         }
         split8(v1, t1h[ks], t1l[ks]);
         t2[ks] = cvt8(v2);
@@ -449,239 +454,280 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
 }
 
 // ---------------------------------------------------------------------------
-// scan kernel: one workgroup per (16-column slice, value head, layer*row).
+// scan kernel: one workgroup of two waves per (16-column slice, value head,
+// layer*row).
+//  wave 0 (state wave) carries the slice of H (d_k x 16, fp32, C layout) in
+//    VGPRs and runs the recurrence: U = U~ - W~ H, S = diag(s) U,
+//    H' = gC H + K^T S.  Because W~, K^T and the S operand use the permuted
+//    k order, every operand it needs is built from its own C-layout
+//    registers: no LDS and no barrier on the recurrence chain.
+//  wave 1 (output wave) computes O = diag(qs) Q H + P U for the chunk from
+//    the H and U fragments the state wave publishes in a two-slot LDS ring.
+// One barrier per chunk hands a ring slot from the state wave to the output
+// wave; the output wave finishes reading slot c%2 before it reaches the next
+// barrier, after which the state wave may overwrite it.
 template <int DK, int DV>
-struct ScanFrags {
-    static constexpr int KS = DK / 32;
-    static constexpr int MQ = (DK / 16 + 3) / 4;   // H' row tiles per wave
-    uint4 wt[KS];        // W~ rows of this wave's token tile (permuted d_k)
-    uint4 q[KS];         // raw Q rows of this wave's token tile (standard d_k)
-    uint4 ph[2], pl[2];  // P rows (permuted tokens)
-    uint4 kt[MQ][2];     // K^T rows of this wave's state tiles (permuted tokens)
-    f32x4 ut;            // U~ tile
-    f32x4 qs, ks;        // per-row output / update scalings
+struct StateFrags {
+    static constexpr int KS = DK / 32, NA = DK / 16;
+    uint4 wt[4][KS];     // W~ rows (4 token tiles, permuted d_k)
+    uint4 kt[NA][2];     // K^T rows (d_k tiles, permuted tokens)
+    f32x4 ut[4];         // U~ tiles of this column slice
+    f32x4 ks[4];         // update scalings of the token rows
     float gC;
 };
 
 template <int DK, int DV>
-__device__ __forceinline__ void scan_load(ScanFrags<DK, DV>& f, const char* rec, const uint16_t* yq,
-                                          int w, int lane, int cs)
+__device__ __forceinline__ void state_load(StateFrags<DK, DV>& f, const char* rec, int cs, int lane)
 {
     using R = Rec<DK, DV>;
+    const int fq = (lane >> 4) * 4;
 #pragma unroll
-    for (int ks = 0; ks < R::KS; ++ks) {
-        f.wt[ks] = *reinterpret_cast<const uint4*>(rec + R::WT + ((w * R::KS + ks) * 64 + lane) * 16);
-        f.q[ks] = *reinterpret_cast<const uint4*>(yq + 32 * ks);
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+        for (int ks = 0; ks < R::KS; ++ks)
+            f.wt[tb][ks] = *reinterpret_cast<const uint4*>(rec + R::WT + ((tb * R::KS + ks) * 64 + lane) * 16);
+        f.ut[tb] = *reinterpret_cast<const f32x4*>(rec + R::UT + ((tb * (DV / 16) + cs) * 64 + lane) * 16);
+        f.ks[tb] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(rec + R::VEC) + CH + 16 * tb + fq);
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        f.ph[ks] = *reinterpret_cast<const uint4*>(rec + R::PH + ((w * 2 + ks) * 64 + lane) * 16);
-        f.pl[ks] = *reinterpret_cast<const uint4*>(rec + R::PL + ((w * 2 + ks) * 64 + lane) * 16);
-    }
-#pragma unroll
-    for (int qq = 0; qq < ScanFrags<DK, DV>::MQ; ++qq) {
-        const int mt = min(w + 4 * qq, DK / 16 - 1);
+    for (int a = 0; a < DK / 16; ++a)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            f.kt[qq][ks] = *reinterpret_cast<const uint4*>(rec + R::KT + ((mt * 2 + ks) * 64 + lane) * 16);
-    }
-    f.ut = *reinterpret_cast<const f32x4*>(rec + R::UT + ((w * (DV / 16) + cs) * 64 + lane) * 16);
-    const float* vec = reinterpret_cast<const float*>(rec + R::VEC);
-    const int fq = (lane >> 4) * 4;
-    f.qs = *reinterpret_cast<const f32x4*>(vec + 16 * w + fq);
-    f.ks = *reinterpret_cast<const f32x4*>(vec + CH + 16 * w + fq);
-    f.gC = vec[2 * CH];
+            f.kt[a][ks] = *reinterpret_cast<const uint4*>(rec + R::KT + ((a * 2 + ks) * 64 + lane) * 16);
+    f.gC = reinterpret_cast<const float*>(rec + R::VEC)[2 * CH];
 }
 
-// A permuted-k B fragment from a [col][k] bf16 row: k = kb + 4q..+4 and kb + 16 + 4q..+4.
-__device__ __forceinline__ uint4 perm_b(const uint16_t* rowp, int kb, int gq)
+template <int DK, int DV>
+struct OutFrags {
+    static constexpr int KS = DK / 32;
+    uint4 q[4][KS];      // raw Q rows (4 token tiles, permuted d_k)
+    uint4 ph[4][2], pl[4][2];   // P rows (permuted tokens)
+    f32x4 qs[4];         // output scalings of the token rows
+};
+
+template <int DK, int DV>
+__device__ __forceinline__ void out_load(OutFrags<DK, DV>& f, const char* rec, const uint16_t* yq, size_t ystride,
+                                         int T, int t0, int lane)
 {
-    const uint2 a = *reinterpret_cast<const uint2*>(rowp + kb + 4 * gq);
-    const uint2 b = *reinterpret_cast<const uint2*>(rowp + kb + 16 + 4 * gq);
-    return make_uint4(a.x, a.y, b.x, b.y);
+    using R = Rec<DK, DV>;
+    const int fr = lane & 15, gq = lane >> 4, fq = gq * 4;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        const uint16_t* row = yq + static_cast<size_t>(min(t0 + 16 * tb + fr, T - 1)) * ystride;
+#pragma unroll
+        for (int ks = 0; ks < R::KS; ++ks) {
+            const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * ks + 4 * gq);
+            const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * ks + 16 + 4 * gq);
+            f.q[tb][ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            f.ph[tb][ks] = *reinterpret_cast<const uint4*>(rec + R::PH + ((tb * 2 + ks) * 64 + lane) * 16);
+            f.pl[tb][ks] = *reinterpret_cast<const uint4*>(rec + R::PL + ((tb * 2 + ks) * 64 + lane) * 16);
+        }
+        f.qs[tb] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(rec + R::VEC) + 16 * tb + fq);
+    }
 }
 
 template <int DK>
-struct ScanShared {
-    uint16_t (*HTh)[16][DK + 8];
-    uint16_t (*HTl)[16][DK + 8];
-    uint16_t (*UTh)[TP];
-    uint16_t (*UTl)[TP];
-    uint16_t (*STh)[TP];
-    uint16_t (*STl)[TP];
+struct Ring {
+    uint4 hh[2][DK / 32][64];   // H hi B-frags (permuted d_k), two slots
+    uint4 hl[2][DK / 32][64];   // H lo
+    uint4 uh[2][2][64];         // U hi B-frags (permuted tokens)
+    uint4 ul[2][2][64];         // U lo
 };
 
-// One chunk of the scan for one wave: U, then O and H'.  FULL: all 64
-// tokens of the chunk exist (no bounds test on the output stores).
-template <int DK, int DV, int OUT, bool FULL>
-__device__ __forceinline__ void scan_chunk(const PrefillParams& p, const ScanFrags<DK, DV>& cur,
-                                           f32x4 (&h)[ScanFrags<DK, DV>::MQ], const ScanShared<DK>& sm,
-                                           int c, int hv, int lb, int col, int w, int lane)
+// split two stacked C tiles into hi and lo permuted-k fragments
+__device__ __forceinline__ void split_c(const f32x4& lo, const f32x4& hi, uint4& fh, uint4& fl)
 {
-    using F = ScanFrags<DK, DV>;
-    const int pb = c & 1;
-    const int fr = lane & 15, gq = lane >> 4, fk = gq * 8, fq = gq * 4;
-    // W~ H (permuted d_k) and Q H (standard d_k, hi and lo) on the state at the chunk start
-    f32x4 wh = {0.f, 0.f, 0.f, 0.f}, qh = {0.f, 0.f, 0.f, 0.f}, ql = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < F::KS; ++ks) {
-        const uint4 hp = perm_b(&sm.HTh[pb][fr][0], 32 * ks, gq);
-        const uint4 hb = *reinterpret_cast<const uint4*>(&sm.HTh[pb][fr][32 * ks + fk]);
-        const uint4 hl = *reinterpret_cast<const uint4*>(&sm.HTl[pb][fr][32 * ks + fk]);
-        wh = mfma(cur.wt[ks], hp, wh);
-        qh = mfma(cur.q[ks], hb, qh);
-        ql = mfma(cur.q[ks], hl, ql);
-    }
-    // U = U~ - W~ H; S = diag(s) U; both to LDS, split, transposed
-    float u[4], sv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        u[j] = cur.ut[j] - wh[j];
-        sv[j] = cur.ks[j] * u[j];
-    }
-    uint32_t uh0, ul0, uh1, ul1, sh0, sl0, sh1, sl1;
-    split2(u[0], u[1], uh0, ul0);
-    split2(u[2], u[3], uh1, ul1);
-    split2(sv[0], sv[1], sh0, sl0);
-    split2(sv[2], sv[3], sh1, sl1);
-    *reinterpret_cast<uint2*>(&sm.UTh[fr][16 * w + fq]) = make_uint2(uh0, uh1);
-    *reinterpret_cast<uint2*>(&sm.UTl[fr][16 * w + fq]) = make_uint2(ul0, ul1);
-    *reinterpret_cast<uint2*>(&sm.STh[fr][16 * w + fq]) = make_uint2(sh0, sh1);
-    *reinterpret_cast<uint2*>(&sm.STl[fr][16 * w + fq]) = make_uint2(sl0, sl1);
-    __syncthreads();
-
-    // O = diag(qs) Q H + P U and H' = gC H + K^T S (P, K^T, U, S over the
-    // permuted token order), as independent MFMA chains.
-    f32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = cur.qs[j] * (qh[j] + ql[j]);
-    f32x4 acc[F::MQ];
-#pragma unroll
-    for (int qq = 0; qq < F::MQ; ++qq)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[qq][j] = cur.gC * h[qq][j];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const uint4 bh = perm_b(&sm.UTh[fr][0], 32 * ks, gq);
-        const uint4 bl = perm_b(&sm.UTl[fr][0], 32 * ks, gq);
-        const uint4 sbh = perm_b(&sm.STh[fr][0], 32 * ks, gq);
-        const uint4 sbl = perm_b(&sm.STl[fr][0], 32 * ks, gq);
-        o = mfma(cur.ph[ks], bh, o);
-#pragma unroll
-        for (int qq = 0; qq < F::MQ; ++qq) acc[qq] = mfma(cur.kt[qq][ks], sbh, acc[qq]);
-        o = mfma(cur.ph[ks], bl, o);
-#pragma unroll
-        for (int qq = 0; qq < F::MQ; ++qq) acc[qq] = mfma(cur.kt[qq][ks], sbl, acc[qq]);
-        o = mfma(cur.pl[ks], bh, o);
-    }
-#pragma unroll
-    for (int qq = 0; qq < F::MQ; ++qq) {
-        const int mt = w + 4 * qq;
-        if (mt < DK / 16) {
-            h[qq] = acc[qq];
-            uint32_t hh0, hl0, hh1, hl1;
-            split2(acc[qq][0], acc[qq][1], hh0, hl0);
-            split2(acc[qq][2], acc[qq][3], hh1, hl1);
-            *reinterpret_cast<uint2*>(&sm.HTh[pb ^ 1][fr][16 * mt + fq]) = make_uint2(hh0, hh1);
-            *reinterpret_cast<uint2*>(&sm.HTl[pb ^ 1][fr][16 * mt + fq]) = make_uint2(hl0, hl1);
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int t = c * CH + 16 * w + fq + j;
-        if (FULL || t < p.T) {
-            const size_t oi = ((static_cast<size_t>(lb) * p.T + t) * p.HV + hv) * DV + col;
-            if constexpr (OUT == ACT_BF16) static_cast<uint16_t*>(p.o)[oi] = f32_to_bf16_bits(o[j]);
-            else static_cast<float*>(p.o)[oi] = o[j];
-        }
-    }
-    __syncthreads();
+    const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    split8(v, fh, fl);
 }
 
 template <int DK, int DV, int OUT>
-__global__ __launch_bounds__(NTHR) void prefill_scan_kernel(PrefillParams p)
+__device__ __forceinline__ void out_chunk(const PrefillParams& p, const OutFrags<DK, DV>& f, Ring<DK>& ring,
+                                          int c, int hv, int lb, int col, int lane)
+{
+    constexpr int KS = DK / 32;
+    const int slot = c & 1;
+    const int fq = (lane >> 4) * 4;
+    uint4 hh[KS], hl[KS], uh[2], ul[2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        hh[ks] = ring.hh[slot][ks][lane];
+        hl[ks] = ring.hl[slot][ks][lane];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        uh[ks] = ring.uh[slot][ks][lane];
+        ul[ks] = ring.ul[slot][ks][lane];
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qa = mfma(f.q[tb][ks], hh[ks], qa);
+            qb = mfma(f.q[tb][ks], hl[ks], qb);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            pu = mfma(f.ph[tb][ks], uh[ks], pu);
+            pu = mfma(f.ph[tb][ks], ul[ks], pu);
+            pu = mfma(f.pl[tb][ks], uh[ks], pu);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = c * CH + 16 * tb + fq + j;
+            if (t < p.T) {
+                const float o = f.qs[tb][j] * (qa[j] + qb[j]) + pu[j];
+                const size_t oi = ((static_cast<size_t>(lb) * p.T + t) * p.HV + hv) * DV + col;
+                if constexpr (OUT == ACT_BF16) static_cast<uint16_t*>(p.o)[oi] = f32_to_bf16_bits(o);
+                else static_cast<float*>(p.o)[oi] = o;
+            }
+        }
+    }
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void state_chunk(const StateFrags<DK, DV>& f, f32x4 (&h)[DK / 16], Ring<DK>& ring,
+                                            int c, int lane)
+{
+    constexpr int KS = DK / 32, NA = DK / 16;
+    const int slot = c & 1;
+    // H as permuted-d_k B fragments (hi for W~ H; hi and lo go to the output wave)
+    uint4 hh[KS], hl[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        split_c(h[2 * ks], h[2 * ks + 1], hh[ks], hl[ks]);
+        ring.hh[slot][ks][lane] = hh[ks];
+        ring.hl[slot][ks][lane] = hl[ks];
+    }
+    // U = U~ - W~ H and S = diag(s) U for the 4 token tiles
+    f32x4 u[4], sv[4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma(f.wt[tb][ks], hh[ks], acc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u[tb][j] = f.ut[tb][j] - acc[j];
+            sv[tb][j] = f.ks[tb][j] * u[tb][j];
+        }
+    }
+    uint4 sh[2], sl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        uint4 a, b;
+        split_c(u[2 * ks], u[2 * ks + 1], a, b);
+        ring.uh[slot][ks][lane] = a;
+        ring.ul[slot][ks][lane] = b;
+        split_c(sv[2 * ks], sv[2 * ks + 1], sh[ks], sl[ks]);
+    }
+    // H' = gC H + K^T S
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+        f32x4 acc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = f.gC * h[a][j];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            acc = mfma(f.kt[a][ks], sh[ks], acc);
+            acc = mfma(f.kt[a][ks], sl[ks], acc);
+        }
+        h[a] = acc;
+    }
+}
+
+template <int DK, int DV, int OUT>
+__global__ __launch_bounds__(128) void prefill_scan_kernel(PrefillParams p)
 {
     using R = Rec<DK, DV>;
-    using F = ScanFrags<DK, DV>;
-    constexpr int HP = DK + 8;
-    __shared__ __align__(16) uint16_t HTh[2][16][HP];   // H^T hi, ping-pong
-    __shared__ __align__(16) uint16_t HTl[2][16][HP];   // H^T lo
-    __shared__ __align__(16) uint16_t UTh[16][TP];      // U^T hi / lo
-    __shared__ __align__(16) uint16_t UTl[16][TP];
-    __shared__ __align__(16) uint16_t STh[16][TP];      // (diag(s) U)^T hi / lo
-    __shared__ __align__(16) uint16_t STl[16][TP];
+    __shared__ __align__(16) Ring<DK> ring;
 
-    const int cs = blockIdx.x;
-    const int hv = blockIdx.y;
-    const int lb = blockIdx.z;
+    // ---- block -> (layer*row, qk head, value head, column slice), XCD-aware:
+    // workgroups go round-robin over the 8 XCDs, so the index is remapped to
+    // put every slice of the value heads of one qk head on one XCD, where
+    // they share the chunk records and q rows through its L2.
+    constexpr int NS = DV / 16;
+    const int gsz = p.HV / p.HK;
+    const int per_group = gsz * NS;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7;
+    const int sg = bid >> 3;
+    const int r_in = sg % per_group;
+    const int grp = (sg / per_group) * 8 + xcd;
+    if (grp >= p.L * p.B * p.HK) return;
+    const int m = grp % p.HK;
+    const int lb = grp / p.HK;
+    const int hv = m * gsz + r_in / NS;
+    const int cs = r_in % NS;
     const int NC = (p.T + CH - 1) / CH;
-    const int m = hv / (p.HV / p.HK);
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int w = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
     const int fr = lane & 15;
-    const int gq = lane >> 4;
-    const int fk = gq * 8;
-    const int fq = gq * 4;
+    const int fq = (lane >> 4) * 4;
 
     const int slot = p.cur ? p.cur[lb] : 0;
     if (slot < 0 || slot >= p.S) {
-        if (tid == 0 && cs == 0 && p.err) atomicOr(p.err, ERR_SLOT);
+        if (threadIdx.x == 0 && cs == 0 && p.err) atomicOr(p.err, ERR_SLOT);
         return;
     }
-    float* st = p.state + ((static_cast<size_t>(lb) * p.S + slot) * p.HV + hv) * DK * DV;
     const int col = 16 * cs + fr;
-
-    // the state slice: wave w owns row tiles w, w+4, ... in C layout
-    f32x4 h[F::MQ];
-#pragma unroll
-    for (int qq = 0; qq < F::MQ; ++qq) {
-        const int mt = w + 4 * qq;
-        if (mt < DK / 16) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) h[qq][j] = st[(16 * mt + fq + j) * DV + col];
-            uint32_t hh0, hl0, hh1, hl1;
-            split2(h[qq][0], h[qq][1], hh0, hl0);
-            split2(h[qq][2], h[qq][3], hh1, hl1);
-            *reinterpret_cast<uint2*>(&HTh[0][fr][16 * mt + fq]) = make_uint2(hh0, hh1);
-            *reinterpret_cast<uint2*>(&HTl[0][fr][16 * mt + fq]) = make_uint2(hl0, hl1);
-        }
-    }
-    __syncthreads();
-
     const char* recs = static_cast<const char*>(p.ws) + (static_cast<size_t>(lb) * p.HV + hv) * NC * R::BYTES;
-    const uint16_t* y = static_cast<const uint16_t*>(p.y);
-    auto qrow = [&](int c) {
-        const int t = min(c * CH + 16 * w + fr, p.T - 1);
-        return y + (static_cast<size_t>(lb) * p.T + t) * p.C + static_cast<size_t>(m) * DK + fk;
-    };
 
-    ScanShared<DK> sm{HTh, HTl, UTh, UTl, STh, STl};
-    // Ping-pong fragment sets; every chunk but the last is full, so its
-    // output stores carry no branch and the next chunk's prefetch can be
-    // waited for without waiting on them.
-    F fa, fb;
-    scan_load<DK, DV>(fa, recs, qrow(0), w, lane, cs);
-    int c = 0;
-    for (; c + 2 < NC; c += 2) {
-        scan_load<DK, DV>(fb, recs + static_cast<size_t>(c + 1) * R::BYTES, qrow(c + 1), w, lane, cs);
-        scan_chunk<DK, DV, OUT, true>(p, fa, h, sm, c, hv, lb, col, w, lane);
-        scan_load<DK, DV>(fa, recs + static_cast<size_t>(c + 2) * R::BYTES, qrow(c + 2), w, lane, cs);
-        scan_chunk<DK, DV, OUT, true>(p, fb, h, sm, c + 1, hv, lb, col, w, lane);
-    }
-    if (c + 1 < NC) {
-        scan_load<DK, DV>(fb, recs + static_cast<size_t>(c + 1) * R::BYTES, qrow(c + 1), w, lane, cs);
-        scan_chunk<DK, DV, OUT, true>(p, fa, h, sm, c, hv, lb, col, w, lane);
-        scan_chunk<DK, DV, OUT, false>(p, fb, h, sm, c + 1, hv, lb, col, w, lane);
+    if (w == 0) {
+        // ---- state wave ----
+        float* st = p.state + ((static_cast<size_t>(lb) * p.S + slot) * p.HV + hv) * DK * DV;
+        f32x4 h[DK / 16];
+#pragma unroll
+        for (int a = 0; a < DK / 16; ++a)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[a][j] = st[(16 * a + fq + j) * DV + col];
+        StateFrags<DK, DV> fa, fb;
+        state_load<DK, DV>(fa, recs, cs, lane);
+        int c = 0;
+        for (; c + 2 <= NC; c += 2) {
+            state_load<DK, DV>(fb, recs + static_cast<size_t>(min(c + 1, NC - 1)) * R::BYTES, cs, lane);
+            state_chunk<DK, DV>(fa, h, ring, c, lane);
+            __syncthreads();
+            if (c + 1 < NC) {
+                state_load<DK, DV>(fa, recs + static_cast<size_t>(min(c + 2, NC - 1)) * R::BYTES, cs, lane);
+                state_chunk<DK, DV>(fb, h, ring, c + 1, lane);
+                __syncthreads();
+            }
+        }
+        if (c < NC) {
+            state_chunk<DK, DV>(fa, h, ring, c, lane);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int a = 0; a < DK / 16; ++a)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st[(16 * a + fq + j) * DV + col] = h[a][j];
     } else {
-        scan_chunk<DK, DV, OUT, false>(p, fa, h, sm, c, hv, lb, col, w, lane);
-    }
-#pragma unroll
-    for (int qq = 0; qq < F::MQ; ++qq) {
-        const int mt = w + 4 * qq;
-        if (mt < DK / 16) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) st[(16 * mt + fq + j) * DV + col] = h[qq][j];
+        // ---- output wave ----
+        const uint16_t* yq = static_cast<const uint16_t*>(p.y) + static_cast<size_t>(lb) * p.T * p.C +
+                             static_cast<size_t>(m) * DK;
+        OutFrags<DK, DV> fa, fb;
+        out_load<DK, DV>(fa, recs, yq, p.C, p.T, 0, lane);
+        int c = 0;
+        for (; c + 2 <= NC; c += 2) {
+            const int c1 = min(c + 1, NC - 1);
+            out_load<DK, DV>(fb, recs + static_cast<size_t>(c1) * R::BYTES, yq, p.C, p.T, c1 * CH, lane);
+            __syncthreads();
+            out_chunk<DK, DV, OUT>(p, fa, ring, c, hv, lb, col, lane);
+            if (c + 1 < NC) {
+                const int c2 = min(c + 2, NC - 1);
+                out_load<DK, DV>(fa, recs + static_cast<size_t>(c2) * R::BYTES, yq, p.C, p.T, c2 * CH, lane);
+                __syncthreads();
+                out_chunk<DK, DV, OUT>(p, fb, ring, c + 1, hv, lb, col, lane);
+            }
+        }
+        if (c < NC) {
+            __syncthreads();
+            out_chunk<DK, DV, OUT>(p, fa, ring, c, hv, lb, col, lane);
         }
     }
 }
@@ -697,12 +743,15 @@ hipError_t launch_pf(const PrefillParams& p, hipStream_t s)
                        dim3(NTHR), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const long long groups = rows * p.HK;
+    const long long blocks = (groups + 7) / 8 * 8 * (p.HV / p.HK) * (DV / 16);
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (p.out == ACT_BF16)
-        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16>),
-                           dim3(DV / 16, p.HV, static_cast<unsigned>(rows)), dim3(NTHR), 0, s, p);
+        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16>), dim3(static_cast<unsigned>(blocks)), dim3(128),
+                           0, s, p);
     else
-        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32>),
-                           dim3(DV / 16, p.HV, static_cast<unsigned>(rows)), dim3(NTHR), 0, s, p);
+        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32>), dim3(static_cast<unsigned>(blocks)), dim3(128),
+                           0, s, p);
     return hipGetLastError();
 }
 

@@ -59,7 +59,8 @@ def oracle_prefill(sh, inp, T=None, state=None):
 
 @pytest.mark.parametrize("T,DK,DV,HV,HK", [(150, 64, 64, 4, 2), (1, 128, 128, 2, 1),
                                            (13, 32, 16, 2, 2), (64, 128, 32, 2, 1),
-                                           (65, 64, 128, 4, 1), (1000, 128, 128, 2, 1)])
+                                           (65, 64, 128, 4, 1), (1000, 128, 128, 2, 1),
+                                           (640, 32, 16, 8, 4)])
 def test_prefill_shapes_ragged(T, DK, DV, HV, HK):
     sh = W.Shape("pf", L=1, B=2, T=T, HV=HV, HK=HK, DK=DK, DV=DV, S=2)
     inp = W.prefill_inputs(sh, seed=3000 + T + DK + DV)
