@@ -5,7 +5,9 @@
 Every HIP source under csrc/ is compiled and linked into one shared library
 next to this file.  Packed-fp32 VALU instructions are disabled on the device
 (-packed-fp32-ops off); hipcc's host pass warns that it does not know that
-feature, which is harmless.
+feature, which is harmless.  MFMA accumulators are kept in ordinary VGPRs
+where possible (-amdgpu-mfma-vgpr-form), so the fp32 state that the prefill
+scan updates with both VALU and MFMA is not copied between register files.
 """
 from __future__ import annotations
 
@@ -36,6 +38,7 @@ def build(verbose: bool = False) -> str:
            "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)

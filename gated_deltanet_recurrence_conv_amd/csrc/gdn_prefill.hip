@@ -30,8 +30,8 @@
 //  scan (one workgroup per 16 columns of a head and row): the sequential part.  Each
 //       workgroup owns 16 columns of one head's state (the d_v columns are
 //       independent recurrences): one wave runs the recurrence with the state
-//       in VGPRs, a second wave computes the outputs; both prefetch the next
-//       chunk's fragments while they compute.
+//       in VGPRs, two more compute the outputs; all prefetch the next chunk's
+//       fragments while they compute.
 //
 // MFMA fragment layout (16x16x32 bf16, wave64): A (16 x 32): lane l holds row
 // l%16, k = 8*(l/16)..+8; B (32 x 16): lane l holds column l%16, k =
@@ -58,7 +58,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;      // chunk length
 constexpr int NTHR = 256;   // 4 waves
-constexpr int TP = CH + 8;  // padded row of a [.][64] bf16 LDS tile
 
 __device__ __forceinline__ f32x4 mfma(const uint4& a, const uint4& b, f32x4 c)
 {
@@ -103,7 +102,8 @@ struct Rec {
     static constexpr size_t PH = UT + 4 * (DV / 16) * 64 * 16;   // P hi A-frags [4][2][64] x 16 B (permuted tokens)
     static constexpr size_t PL = PH + 4 * 2 * 64 * 16;           // P lo
     static constexpr size_t KT = PL + 4 * 2 * 64 * 16;           // K^T A-frags [DK/16][2][64] x 16 B (permuted tokens)
-    static constexpr size_t VEC = KT + (DK / 16) * 2 * 64 * 16;  // qs[64], ks[64], gC
+    static constexpr size_t QA = KT + (DK / 16) * 2 * 64 * 16;   // Q A-frags [4][KS][64] x 16 B (standard d_k order)
+    static constexpr size_t VEC = QA + 4 * KS * 64 * 16;         // qs[64], ks[64], gC
     static constexpr size_t BYTES = VEC + 3 * 64 * 4;
 };
 
@@ -239,6 +239,10 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
     if (r_me >= n)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) qf[ks] = make_uint4(0, 0, 0, 0);
+    char* rec = static_cast<char*>(p.ws) + ((static_cast<size_t>(lb) * p.HV + hv) * NC + c) * R::BYTES;
+    // raw Q rows of token tile w: the A operand of the output products
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<uint4*>(rec + R::QA + ((w * KS + ks) * 64 + lane) * 16) = qf[ks];
     float sq = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -283,7 +287,6 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
         }
     }
     // ---- K^T and V in token-permuted fragment order via 0/1 selection products ----
-    char* rec = static_cast<char*>(p.ws) + ((static_cast<size_t>(lb) * p.HV + hv) * NC + c) * R::BYTES;
     {
         const uint4 sel0 = select_frag(lane, 0), sel1 = select_frag(lane, 1);
         for (int db = w; db < DK / 16; db += 4) {
@@ -454,194 +457,281 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
 }
 
 // ---------------------------------------------------------------------------
-// scan kernel: one workgroup of two waves per (16-column slice, value head,
+// scan kernel: one workgroup of three waves per (16-column slice, value head,
 // layer*row).
 //  wave 0 (state wave) carries the slice of H (d_k x 16, fp32, C layout) in
 //    VGPRs and runs the recurrence: U = U~ - W~ H, S = diag(s) U,
 //    H' = gC H + K^T S.  Because W~, K^T and the S operand use the permuted
 //    k order, every operand it needs is built from its own C-layout
 //    registers: no LDS and no barrier on the recurrence chain.
-//  wave 1 (output wave) computes O = diag(qs) Q H + P U for the chunk from
-//    the H and U fragments the state wave publishes in a two-slot LDS ring.
+//  waves 1 and 2 (output waves) compute O = diag(qs) Q H + P U for two of
+//    the four 16-token tiles each, tiles {0, 3} and {1, 2}: P is lower
+//    triangular, so tiles 0 and 1 need only the first 32 tokens of U and
+//    the two pairs carry equal work.  They take the fp32 H and U the state
+//    wave publishes in a two-slot LDS ring and split them into bf16 hi/lo
+//    operands themselves.
 // One barrier per chunk hands a ring slot from the state wave to the output
-// wave; the output wave finishes reading slot c%2 before it reaches the next
-// barrier, after which the state wave may overwrite it.
+// waves; they finish reading slot c%2 before they reach the next barrier,
+// after which the state wave may overwrite it.
+//
+// Every load and store goes through a buffer resource whose base moves with
+// the chunk, so a per-access address is a lane-constant VGPR plus constants
+// (no 64-bit address arithmetic per load).  All operands come from the chunk
+// record in fragment order (1 KB contiguous per wave load).  For the output
+// the row index sits in the VGPR offset and the resource's byte range ends
+// inside the last valid token row, so in the tail chunk the stores of rows
+// past the prompt are dropped by the range check.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int RSRC_WORD3 = 0x00020000;   // raw (stride 0) buffer, 32-bit data format
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), RSRC_WORD3);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint2 bload8(rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ f32x4 as_f4(const uint4& v)
+{
+    return __builtin_bit_cast(f32x4, v);
+}
+
+// W~ is single-buffered: it is consumed by the first products of a chunk and
+// reloaded for the next chunk right after them.  K^T, U~ and the scalings are
+// double-buffered (K^T is consumed at the end of the chunk).
+template <int DK>
+struct WFrags {
+    uint4 wt[4][DK / 32];   // W~ rows (4 token tiles, permuted d_k)
+};
 template <int DK, int DV>
-struct StateFrags {
-    static constexpr int KS = DK / 32, NA = DK / 16;
-    uint4 wt[4][KS];     // W~ rows (4 token tiles, permuted d_k)
-    uint4 kt[NA][2];     // K^T rows (d_k tiles, permuted tokens)
-    f32x4 ut[4];         // U~ tiles of this column slice
-    f32x4 ks[4];         // update scalings of the token rows
-    float gC;
+struct KFrags {
+    uint4 kt[DK / 16][2];   // K^T rows (d_k tiles, permuted tokens)
+    uint4 ut[4];            // U~ tiles of this column slice (fp32 C layout)
+    uint4 ks[4];            // update scalings of the token rows (fp32)
+    float gC;               // chunk decay
 };
 
 template <int DK, int DV>
-__device__ __forceinline__ void state_load(StateFrags<DK, DV>& f, const char* rec, int cs, int lane)
+__device__ __forceinline__ void w_load(WFrags<DK>& f, rsrc_t r, int lane16)
 {
     using R = Rec<DK, DV>;
-    const int fq = (lane >> 4) * 4;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < R::KS; ++ks) f.wt[tb][ks] = bload16(r, lane16, R::WT + (tb * R::KS + ks) * 1024);
+}
+
+template <int DK, int DV>
+__device__ __forceinline__ void k_load(KFrags<DK, DV>& f, rsrc_t r, int lane16, int vq16, int cs)
+{
+    using R = Rec<DK, DV>;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-        for (int ks = 0; ks < R::KS; ++ks)
-            f.wt[tb][ks] = *reinterpret_cast<const uint4*>(rec + R::WT + ((tb * R::KS + ks) * 64 + lane) * 16);
-        f.ut[tb] = *reinterpret_cast<const f32x4*>(rec + R::UT + ((tb * (DV / 16) + cs) * 64 + lane) * 16);
-        f.ks[tb] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(rec + R::VEC) + CH + 16 * tb + fq);
+        f.ut[tb] = bload16(r, lane16, R::UT + (tb * (DV / 16) + cs) * 1024);
+        f.ks[tb] = bload16(r, vq16, R::VEC + (CH + 16 * tb) * 4);
     }
 #pragma unroll
     for (int a = 0; a < DK / 16; ++a)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            f.kt[a][ks] = *reinterpret_cast<const uint4*>(rec + R::KT + ((a * 2 + ks) * 64 + lane) * 16);
-    f.gC = reinterpret_cast<const float*>(rec + R::VEC)[2 * CH];
-}
-
-template <int DK, int DV>
-struct OutFrags {
-    static constexpr int KS = DK / 32;
-    uint4 q[4][KS];      // raw Q rows (4 token tiles, permuted d_k)
-    uint4 ph[4][2], pl[4][2];   // P rows (permuted tokens)
-    f32x4 qs[4];         // output scalings of the token rows
-};
-
-template <int DK, int DV>
-__device__ __forceinline__ void out_load(OutFrags<DK, DV>& f, const char* rec, const uint16_t* yq, size_t ystride,
-                                         int T, int t0, int lane)
-{
-    using R = Rec<DK, DV>;
-    const int fr = lane & 15, gq = lane >> 4, fq = gq * 4;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        const uint16_t* row = yq + static_cast<size_t>(min(t0 + 16 * tb + fr, T - 1)) * ystride;
-#pragma unroll
-        for (int ks = 0; ks < R::KS; ++ks) {
-            const uint2 lo = *reinterpret_cast<const uint2*>(row + 32 * ks + 4 * gq);
-            const uint2 hi = *reinterpret_cast<const uint2*>(row + 32 * ks + 16 + 4 * gq);
-            f.q[tb][ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            f.ph[tb][ks] = *reinterpret_cast<const uint4*>(rec + R::PH + ((tb * 2 + ks) * 64 + lane) * 16);
-            f.pl[tb][ks] = *reinterpret_cast<const uint4*>(rec + R::PL + ((tb * 2 + ks) * 64 + lane) * 16);
-        }
-        f.qs[tb] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(rec + R::VEC) + 16 * tb + fq);
-    }
+        for (int ks = 0; ks < 2; ++ks) f.kt[a][ks] = bload16(r, lane16, R::KT + (a * 2 + ks) * 1024);
+    f.gC = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 0, R::VEC + 2 * CH * 4, 0));
 }
 
 template <int DK>
 struct Ring {
-    uint4 hh[2][DK / 32][64];   // H hi B-frags (permuted d_k), two slots
-    uint4 hl[2][DK / 32][64];   // H lo
-    uint4 uh[2][2][64];         // U hi B-frags (permuted tokens)
-    uint4 ul[2][2][64];         // U lo
+    f32x4 h[2][DK / 16][64];   // H at the start of the chunk (C tiles), two slots
+    f32x4 u[2][4][64];         // U of the chunk (C tiles)
 };
 
-// split two stacked C tiles into hi and lo permuted-k fragments
-__device__ __forceinline__ void split_c(const f32x4& lo, const f32x4& hi, uint4& fh, uint4& fl)
-{
-    const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    split8(v, fh, fl);
-}
-
-template <int DK, int DV, int OUT>
-__device__ __forceinline__ void out_chunk(const PrefillParams& p, const OutFrags<DK, DV>& f, Ring<DK>& ring,
-                                          int c, int hv, int lb, int col, int lane)
-{
-    constexpr int KS = DK / 32;
-    const int slot = c & 1;
-    const int fq = (lane >> 4) * 4;
-    uint4 hh[KS], hl[KS], uh[2], ul[2];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        hh[ks] = ring.hh[slot][ks][lane];
-        hl[ks] = ring.hl[slot][ks][lane];
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        uh[ks] = ring.uh[slot][ks][lane];
-        ul[ks] = ring.ul[slot][ks][lane];
-    }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            qa = mfma(f.q[tb][ks], hh[ks], qa);
-            qb = mfma(f.q[tb][ks], hl[ks], qb);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            pu = mfma(f.ph[tb][ks], uh[ks], pu);
-            pu = mfma(f.ph[tb][ks], ul[ks], pu);
-            pu = mfma(f.pl[tb][ks], uh[ks], pu);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = c * CH + 16 * tb + fq + j;
-            if (t < p.T) {
-                const float o = f.qs[tb][j] * (qa[j] + qb[j]) + pu[j];
-                const size_t oi = ((static_cast<size_t>(lb) * p.T + t) * p.HV + hv) * DV + col;
-                if constexpr (OUT == ACT_BF16) static_cast<uint16_t*>(p.o)[oi] = f32_to_bf16_bits(o);
-                else static_cast<float*>(p.o)[oi] = o;
-            }
-        }
-    }
-}
-
 template <int DK, int DV>
-__device__ __forceinline__ void state_chunk(const StateFrags<DK, DV>& f, f32x4 (&h)[DK / 16], Ring<DK>& ring,
-                                            int c, int lane)
+__device__ __forceinline__ void state_chunk(WFrags<DK>& wf, const KFrags<DK, DV>& f, rsrc_t rnext,
+                                            f32x4 (&h)[DK / 16], Ring<DK>& ring, int c, int lane)
 {
     constexpr int KS = DK / 32, NA = DK / 16;
     const int slot = c & 1;
-    // H as permuted-d_k B fragments (hi for W~ H; hi and lo go to the output wave)
-    uint4 hh[KS], hl[KS];
+    // publish H; its bf16 rounding is the B operand of W~ H
+    uint4 hh[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        split_c(h[2 * ks], h[2 * ks + 1], hh[ks], hl[ks]);
-        ring.hh[slot][ks][lane] = hh[ks];
-        ring.hl[slot][ks][lane] = hl[ks];
-    }
-    // U = U~ - W~ H and S = diag(s) U for the 4 token tiles
-    f32x4 u[4], sv[4];
+    for (int a = 0; a < NA; ++a) ring.h[slot][a][lane] = h[a];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) hh[ks] = frag_from_c(h[2 * ks], h[2 * ks + 1]);
+    // P = W~ H
+    f32x4 acc[4];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma(f.wt[tb][ks], hh[ks], acc);
+        for (int ks = 0; ks < KS; ++ks) acc[tb] = mfma(wf.wt[tb][ks], hh[ks], acc[tb]);
+    }
+    w_load<DK, DV>(wf, rnext, lane * 16);   // W~ of the next chunk
+    // U = U~ - W~ H, published; S = diag(s) U split into hi + lo
+    f32x4 sv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            u[tb][j] = f.ut[tb][j] - acc[j];
-            sv[tb][j] = f.ks[tb][j] * u[tb][j];
-        }
+    for (int tb = 0; tb < 4; ++tb) {
+        const f32x4 u = as_f4(f.ut[tb]) - acc[tb];
+        ring.u[slot][tb][lane] = u;
+        sv[tb] = as_f4(f.ks[tb]) * u;
     }
     uint4 sh[2], sl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        uint4 a, b;
-        split_c(u[2 * ks], u[2 * ks + 1], a, b);
-        ring.uh[slot][ks][lane] = a;
-        ring.ul[slot][ks][lane] = b;
-        split_c(sv[2 * ks], sv[2 * ks + 1], sh[ks], sl[ks]);
+        const float v[8] = {sv[2 * ks][0], sv[2 * ks][1], sv[2 * ks][2], sv[2 * ks][3],
+                            sv[2 * ks + 1][0], sv[2 * ks + 1][1], sv[2 * ks + 1][2], sv[2 * ks + 1][3]};
+        split8(v, sh[ks], sl[ks]);
     }
     // H' = gC H + K^T S
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
-        f32x4 acc;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = f.gC * h[a][j];
+        f32x4 acc2 = f.gC * h[a];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            acc = mfma(f.kt[a][ks], sh[ks], acc);
-            acc = mfma(f.kt[a][ks], sl[ks], acc);
+            acc2 = mfma(f.kt[a][ks], sh[ks], acc2);
+            acc2 = mfma(f.kt[a][ks], sl[ks], acc2);
         }
-        h[a] = acc;
+        h[a] = acc2;
+    }
+}
+
+// the k-steps of P U that can be nonzero for token tile tb (P is lower triangular)
+constexpr int pu_steps(int tb) { return tb >= 2 ? 2 : 1; }
+
+template <int DK, int DV>
+struct OutFrags {
+    static constexpr int KS = DK / 32;
+    uint4 q[2][KS];             // raw Q rows of the two tiles (standard d_k order)
+    uint4 ph[2][2], pl[2][2];   // P rows (permuted tokens), hi and lo
+    uint4 qs[2];                // output scalings of the token rows (fp32)
+};
+
+template <int DK, int DV, int TA, int TB>
+__device__ __forceinline__ void out_load(OutFrags<DK, DV>& f, rsrc_t rrec, int lane16, int vq16)
+{
+    using R = Rec<DK, DV>;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tb = i ? TB : TA;
+#pragma unroll
+        for (int ks = 0; ks < R::KS; ++ks) f.q[i][ks] = bload16(rrec, lane16, R::QA + (tb * R::KS + ks) * 1024);
+#pragma unroll
+        for (int ks = 0; ks < pu_steps(tb); ++ks) {
+            f.ph[i][ks] = bload16(rrec, lane16, R::PH + (tb * 2 + ks) * 1024);
+            f.pl[i][ks] = bload16(rrec, lane16, R::PL + (tb * 2 + ks) * 1024);
+        }
+        f.qs[i] = bload16(rrec, vq16, R::VEC + 16 * tb * 4);
+    }
+}
+
+template <int DK, int DV, int OUT, int TA, int TB>
+__device__ __forceinline__ void out_chunk(const OutFrags<DK, DV>& f, const Ring<DK>& ring, int c, rsrc_t ro,
+                                          const int (&vo)[2][4], int lane)
+{
+    constexpr int KS = DK / 32;
+    const int slot = c & 1;
+    uint4 hh[KS], hl[KS], uh[2], ul[2];
+    // H rows 32 ks + 8 gq + (0..7) of column fr, the standard k order of Q's
+    // A fragments: rows 4 of C tile 2 ks + gq / 2 held by two lanes of the ring
+    const int gq = lane >> 4, fr = lane & 15;
+    const int l0 = 32 * (gq & 1) + fr;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const f32x4 a = ring.h[slot][2 * ks + (gq >> 1)][l0], b = ring.h[slot][2 * ks + (gq >> 1)][l0 + 16];
+        const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        split8(v, hh[ks], hl[ks]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const f32x4 a = ring.u[slot][2 * ks][lane], b = ring.u[slot][2 * ks + 1][lane];
+        const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        split8(v, uh[ks], ul[ks]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tb = i ? TB : TA;
+        f32x4 qa = {0.f, 0.f, 0.f, 0.f}, qb = {0.f, 0.f, 0.f, 0.f}, pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            qa = mfma(f.q[i][ks], hh[ks], qa);
+            qb = mfma(f.q[i][ks], hl[ks], qb);
+        }
+#pragma unroll
+        for (int ks = 0; ks < pu_steps(tb); ++ks) {
+            pu = mfma(f.ph[i][ks], uh[ks], pu);
+            pu = mfma(f.ph[i][ks], ul[ks], pu);
+            pu = mfma(f.pl[i][ks], uh[ks], pu);
+        }
+        const f32x4 o = as_f4(f.qs[i]) * (qa + qb) + pu;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (OUT == ACT_BF16)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(o[j]), ro, vo[i][j], 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[j]), ro, vo[i][j], 0, 0);
+        }
+    }
+}
+
+// resources of chunk c: its workspace record and its output rows
+struct ChunkRes {
+    rsrc_t rec, o;
+};
+
+template <int DK, int DV, int OUT>
+__device__ __forceinline__ ChunkRes chunk_res(const PrefillParams& p, const char* recs, int c, int lb, int hv)
+{
+    using R = Rec<DK, DV>;
+    constexpr int OSZ = OUT == ACT_BF16 ? 2 : 4;
+    const int t0 = c * CH;
+    const int n = min(CH, p.T - t0);
+    ChunkRes r;
+    r.rec = make_rsrc(recs + static_cast<size_t>(c) * R::BYTES, static_cast<uint32_t>(R::BYTES));
+    const size_t row0 = static_cast<size_t>(lb) * p.T + t0;
+    r.o = make_rsrc(static_cast<const char*>(p.o) + ((row0 * p.HV + hv) * DV) * OSZ,
+                    static_cast<uint32_t>(((n - 1) * p.HV + 1) * DV * OSZ));
+    return r;
+}
+
+template <int DK, int DV, int OUT, int TA, int TB>
+__device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK>& ring, const char* recs, int NC, int lb,
+                                         int hv, int cs, int lane)
+{
+    constexpr int OSZ = OUT == ACT_BF16 ? 2 : 4;
+    const int fr = lane & 15, gq = lane >> 4;
+    const int lane16 = lane * 16, vq16 = gq * 16;
+    int vo[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int tb = i ? TB : TA;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vo[i][j] = ((16 * tb + 4 * gq + j) * p.HV * DV + 16 * cs + fr) * OSZ;
+    }
+    OutFrags<DK, DV> fa, fb;
+    ChunkRes ra = chunk_res<DK, DV, OUT>(p, recs, 0, lb, hv), rb;
+    out_load<DK, DV, TA, TB>(fa, ra.rec, lane16, vq16);
+    int c = 0;
+    for (; c + 2 <= NC; c += 2) {
+        rb = chunk_res<DK, DV, OUT>(p, recs, c + 1, lb, hv);
+        out_load<DK, DV, TA, TB>(fb, rb.rec, lane16, vq16);
+        __syncthreads();
+        out_chunk<DK, DV, OUT, TA, TB>(fa, ring, c, ra.o, vo, lane);
+        const int c2 = min(c + 2, NC - 1);
+        ra = chunk_res<DK, DV, OUT>(p, recs, c2, lb, hv);
+        out_load<DK, DV, TA, TB>(fa, ra.rec, lane16, vq16);
+        __syncthreads();
+        out_chunk<DK, DV, OUT, TA, TB>(fb, ring, c + 1, rb.o, vo, lane);
+    }
+    if (c < NC) {
+        __syncthreads();
+        out_chunk<DK, DV, OUT, TA, TB>(fa, ring, c, ra.o, vo, lane);
     }
 }
 
 template <int DK, int DV, int OUT>
-__global__ __launch_bounds__(128) void prefill_scan_kernel(PrefillParams p)
+__global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
 {
     using R = Rec<DK, DV>;
     __shared__ __align__(16) Ring<DK> ring;
@@ -665,70 +755,54 @@ __global__ __launch_bounds__(128) void prefill_scan_kernel(PrefillParams p)
     const int cs = r_in % NS;
     const int NC = (p.T + CH - 1) / CH;
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
-    const int fr = lane & 15;
-    const int fq = (lane >> 4) * 4;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform role
 
     const int slot = p.cur ? p.cur[lb] : 0;
     if (slot < 0 || slot >= p.S) {
         if (threadIdx.x == 0 && cs == 0 && p.err) atomicOr(p.err, ERR_SLOT);
         return;
     }
-    const int col = 16 * cs + fr;
     const char* recs = static_cast<const char*>(p.ws) + (static_cast<size_t>(lb) * p.HV + hv) * NC * R::BYTES;
 
     if (w == 0) {
         // ---- state wave ----
+        const int fr = lane & 15, fq = (lane >> 4) * 4;
+        const int lane16 = lane * 16, vq16 = (lane >> 4) * 16;
+        const int col = 16 * cs + fr;
         float* st = p.state + ((static_cast<size_t>(lb) * p.S + slot) * p.HV + hv) * DK * DV;
         f32x4 h[DK / 16];
 #pragma unroll
         for (int a = 0; a < DK / 16; ++a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) h[a][j] = st[(16 * a + fq + j) * DV + col];
-        StateFrags<DK, DV> fa, fb;
-        state_load<DK, DV>(fa, recs, cs, lane);
+        auto rec_rsrc = [&](int cc) {
+            return make_rsrc(recs + static_cast<size_t>(min(cc, NC - 1)) * R::BYTES, static_cast<uint32_t>(R::BYTES));
+        };
+        WFrags<DK> wf;
+        KFrags<DK, DV> fa, fb;
+        w_load<DK, DV>(wf, rec_rsrc(0), lane16);
+        k_load<DK, DV>(fa, rec_rsrc(0), lane16, vq16, cs);
         int c = 0;
         for (; c + 2 <= NC; c += 2) {
-            state_load<DK, DV>(fb, recs + static_cast<size_t>(min(c + 1, NC - 1)) * R::BYTES, cs, lane);
-            state_chunk<DK, DV>(fa, h, ring, c, lane);
+            k_load<DK, DV>(fb, rec_rsrc(c + 1), lane16, vq16, cs);
+            state_chunk<DK, DV>(wf, fa, rec_rsrc(c + 1), h, ring, c, lane);
             __syncthreads();
-            if (c + 1 < NC) {
-                state_load<DK, DV>(fa, recs + static_cast<size_t>(min(c + 2, NC - 1)) * R::BYTES, cs, lane);
-                state_chunk<DK, DV>(fb, h, ring, c + 1, lane);
-                __syncthreads();
-            }
+            k_load<DK, DV>(fa, rec_rsrc(c + 2), lane16, vq16, cs);
+            state_chunk<DK, DV>(wf, fb, rec_rsrc(c + 2), h, ring, c + 1, lane);
+            __syncthreads();
         }
         if (c < NC) {
-            state_chunk<DK, DV>(fa, h, ring, c, lane);
+            state_chunk<DK, DV>(wf, fa, rec_rsrc(c), h, ring, c, lane);
             __syncthreads();
         }
 #pragma unroll
         for (int a = 0; a < DK / 16; ++a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) st[(16 * a + fq + j) * DV + col] = h[a][j];
+    } else if (w == 1) {
+        out_wave<DK, DV, OUT, 0, 3>(p, ring, recs, NC, lb, hv, cs, lane);
     } else {
-        // ---- output wave ----
-        const uint16_t* yq = static_cast<const uint16_t*>(p.y) + static_cast<size_t>(lb) * p.T * p.C +
-                             static_cast<size_t>(m) * DK;
-        OutFrags<DK, DV> fa, fb;
-        out_load<DK, DV>(fa, recs, yq, p.C, p.T, 0, lane);
-        int c = 0;
-        for (; c + 2 <= NC; c += 2) {
-            const int c1 = min(c + 1, NC - 1);
-            out_load<DK, DV>(fb, recs + static_cast<size_t>(c1) * R::BYTES, yq, p.C, p.T, c1 * CH, lane);
-            __syncthreads();
-            out_chunk<DK, DV, OUT>(p, fa, ring, c, hv, lb, col, lane);
-            if (c + 1 < NC) {
-                const int c2 = min(c + 2, NC - 1);
-                out_load<DK, DV>(fa, recs + static_cast<size_t>(c2) * R::BYTES, yq, p.C, p.T, c2 * CH, lane);
-                __syncthreads();
-                out_chunk<DK, DV, OUT>(p, fb, ring, c + 1, hv, lb, col, lane);
-            }
-        }
-        if (c < NC) {
-            __syncthreads();
-            out_chunk<DK, DV, OUT>(p, fa, ring, c, hv, lb, col, lane);
-        }
+        out_wave<DK, DV, OUT, 1, 2>(p, ring, recs, NC, lb, hv, cs, lane);
     }
 }
 
@@ -747,10 +821,10 @@ hipError_t launch_pf(const PrefillParams& p, hipStream_t s)
     const long long blocks = (groups + 7) / 8 * 8 * (p.HV / p.HK) * (DV / 16);
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (p.out == ACT_BF16)
-        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16>), dim3(static_cast<unsigned>(blocks)), dim3(128),
+        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16>), dim3(static_cast<unsigned>(blocks)), dim3(192),
                            0, s, p);
     else
-        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32>), dim3(static_cast<unsigned>(blocks)), dim3(128),
+        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32>), dim3(static_cast<unsigned>(blocks)), dim3(192),
                            0, s, p);
     return hipGetLastError();
 }
