@@ -164,7 +164,9 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
     __shared__ __align__(16) uint4 Vf[DV / 16][2][64];    // V B-frags (permuted tokens)
     constexpr int SP = 17;       // fp32 row pitch of the inverse scratch
     __shared__ float Scr[4][2][16][SP];                   // per-wave scratch for the inverse
-    __shared__ float Gs[CH], Bs[CH], Ink[CH];   // Gs: cumulative log2 decay
+    __shared__ __align__(16) float Gs[CH];      // cumulative decay, log2 units
+    __shared__ __align__(16) float Bs[CH];
+    __shared__ __align__(16) float Ink[CH];
     auto Ks = reinterpret_cast<uint16_t(*)[KP]>(r1);
     auto Vs = reinterpret_cast<uint16_t(*)[VP]>(r1 + static_cast<size_t>(CH) * KP * 2);
     float* Af = reinterpret_cast<float*>(r1);
@@ -323,17 +325,24 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
     // ---- A (fp32, LDS), P = scale lower_incl(E o Q^K^T) (split A-frags), per-token vectors ----
     {
         const float g_me = Gs[r_me], b_me = Bs[r_me], ink_me = Ink[r_me];
+        const float sa = b_me * ink_me, sp = p.scale * inq_me;
         float pv[2][8];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+            // this lane's 4 columns i = 16 a + fq + j: one vector read per table
+            const f32x4 gi = *reinterpret_cast<const f32x4*>(&Gs[16 * a + fq]);
+            const f32x4 ki = *reinterpret_cast<const f32x4*>(&Ink[16 * a + fq]);
+            f32x4 arow;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int i = 16 * a + fq + j;
-                const float e = (i <= r_me) ? exp2f(g_me - Gs[i]) : 0.f;
-                const float ink_i = Ink[i];
-                Af[r_me * FP + i] = (i < r_me) ? b_me * e * kk[a][j] * ink_me * ink_i : 0.f;
-                pv[a >> 1][4 * (a & 1) + j] = (i <= r_me) ? p.scale * e * kq[a][j] * inq_me * ink_i : 0.f;
+                // exp2 of G_r - G_i <= 0 on and below the diagonal; the value
+                // above it is discarded by the selects
+                const float e = (i <= r_me) ? __builtin_amdgcn_exp2f(g_me - gi[j]) : 0.f;
+                arow[j] = (i < r_me) ? sa * e * kk[a][j] * ki[j] : 0.f;
+                pv[a >> 1][4 * (a & 1) + j] = sp * e * kq[a][j] * ki[j];
             }
+            *reinterpret_cast<f32x4*>(&Af[r_me * FP + 16 * a + fq]) = arow;
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -349,10 +358,13 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
             vec[CH + lane] = (lane < n) ? exp2f(gl - Gs[lane]) * Ink[lane] : 0.f;
             vec[2 * CH + lane] = exp2f(gl);
         }
-        // upper blocks of T are zero
-        for (int e2 = tid; e2 < CH * CH; e2 += NTHR) {
-            const int rr = e2 >> 6, ii = e2 & 63;
-            if ((ii >> 4) > (rr >> 4)) Tf[rr * FP + ii] = 0.f;
+        // upper blocks of T are zero: thread -> row tid / 4, columns 16 (tid % 4) ..
+        {
+            const int rr = tid >> 2, qb = tid & 3;
+            if (qb > (rr >> 4))
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    *reinterpret_cast<f32x4*>(&Tf[rr * FP + 16 * qb + 4 * e]) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
     __syncthreads();   // A complete
@@ -419,15 +431,21 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
     uint4 t1h[2], t1l[2], t2[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-        const float4 a4 = *reinterpret_cast<const float4*>(&Tf[r_me * FP + 32 * ks + fq]);
-        const float4 b4 = *reinterpret_cast<const float4*>(&Tf[r_me * FP + 32 * ks + 16 + fq]);
-        const float tv[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&Tf[r_me * FP + 32 * ks + fq]);
+        const f32x4 b4 = *reinterpret_cast<const f32x4*>(&Tf[r_me * FP + 32 * ks + 16 + fq]);
+        const f32x4 bl = *reinterpret_cast<const f32x4*>(&Bs[32 * ks + fq]);
+        const f32x4 bh = *reinterpret_cast<const f32x4*>(&Bs[32 * ks + 16 + fq]);
+        const f32x4 gl = *reinterpret_cast<const f32x4*>(&Gs[32 * ks + fq]);
+        const f32x4 gh = *reinterpret_cast<const f32x4*>(&Gs[32 * ks + 16 + fq]);
+        const f32x4 il = *reinterpret_cast<const f32x4*>(&Ink[32 * ks + fq]);
+        const f32x4 ih = *reinterpret_cast<const f32x4*>(&Ink[32 * ks + 16 + fq]);
         float v1[8], v2[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int i = 32 * ks + (e < 4 ? fq + e : 12 + fq + e);
-            v1[e] = tv[e] * Bs[i];
-            v2[e] = v1[e] * exp2f(Gs[i]) * Ink[i];
+        for (int e = 0; e < 4; ++e) {   // tokens 32 ks + fq + e and 32 ks + 16 + fq + e
+            v1[e] = a4[e] * bl[e];
+            v1[4 + e] = b4[e] * bh[e];
+            v2[e] = v1[e] * __builtin_amdgcn_exp2f(gl[e]) * il[e];
+            v2[4 + e] = v1[4 + e] * __builtin_amdgcn_exp2f(gh[e]) * ih[e];
         }
         split8(v1, t1h[ks], t1l[ks]);
         t2[ks] = cvt8(v2);
