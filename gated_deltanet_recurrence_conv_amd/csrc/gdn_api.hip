@@ -123,14 +123,8 @@ gdn_status gdn_conv_step(const gdn_dims* d, const void* x, const void* conv_w, c
     p.active = active;
     p.L = d->L; p.B = d->B; p.T = d->T; p.C = channels(d);
     p.act = d->act; p.out = d->out; p.flags = d->flags;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = from_hip(gdn::launch_conv(p, s));
-    if (st != GDN_OK || !commit_state) return st;
-    WinParams w{};
-    w.x = x; w.conv_state = conv_state; w.active = active; w.err = err;
-    w.L = d->L; w.B = d->B; w.T = d->T; w.S = d->S; w.C = p.C; w.act = d->act;
-    w.mode = gdn::WIN_FULL;
-    return from_hip(gdn::launch_window(w, s));
+    p.commit = commit_state ? 1 : 0;
+    return from_hip(gdn::launch_conv(p, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status gdn_verify(const gdn_dims* d, const void* x, const void* conv_w, const void* conv_b,

@@ -54,9 +54,10 @@ __device__ __forceinline__ void store_vec8(void* base, size_t idx, int dt, const
 }
 
 // ---------------------------------------------------------------------------
-// Conv-window shift.  grid = (ceil(C / (8*256)), L*B); each thread handles 8
-// channels of one (layer, row).  All three source rows are read into
-// registers before the cache is overwritten.
+// Conv-window shift by keep tokens (commit and rewind).  grid =
+// (ceil(C / (8*256)), L*B); each thread handles 8 channels of one (layer,
+// row).  All three source rows are read into registers before the cache is
+// overwritten.
 __global__ __launch_bounds__(256) void window_kernel(WinParams p)
 {
     const int lb = blockIdx.y;
@@ -64,10 +65,7 @@ __global__ __launch_bounds__(256) void window_kernel(WinParams p)
     const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
 
     int shift;
-    if (p.mode == WIN_FULL) {
-        if (p.active && p.active[b] == 0) return;
-        shift = p.T;
-    } else {
+    {
         const int kp = p.keep[b];
         const int slot = p.cur ? p.cur[lb] : 0;
         const bool act = p.mode == WIN_REWIND ? true : (p.active ? p.active[b] != 0 : true);
@@ -124,33 +122,72 @@ hipError_t launch_window(const WinParams& p, hipStream_t s)
 
 // ---------------------------------------------------------------------------
 // Conv step: y for every token.  grid = (ceil(C / (8*CT)), ceil(T / TR), L*B)
-// with CT threads per block; each thread slides a 4-row window down TR tokens
-// for its 8 channels.
+// with CT threads per block; each thread produces TR tokens of its 8
+// channels.  All TR + 3 window rows are loaded up front (row indices past the
+// last token are clamped onto it, their results are not stored), so a
+// thread's loads are all in flight at once instead of one per token.
 constexpr int CONV_CT = 128;
-constexpr int CONV_TR = 8;
+
+// SiLU with the hardware exp2 and reciprocal (each within about 1 ulp):
+// v * 1 / (1 + 2^(-v log2 e)).  Saturates to v and -0 at the extremes.
+__device__ __forceinline__ float silu_hw(float v)
+{
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
+}
 
 template <int ACT>
+__device__ __forceinline__ void to_f32x8(const uint4 (&raw)[ACT == ACT_BF16 ? 1 : 2], float* v)
+{
+    if constexpr (ACT == ACT_BF16) {
+        const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+        const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+    }
+}
+
+template <int ACT, int TR>
 __global__ __launch_bounds__(CONV_CT) void conv_kernel(ConvParams p)
 {
+    constexpr int NV = ACT == ACT_BF16 ? 1 : 2;   // 16-byte vectors per 8 channels
+    constexpr int ESZ = ACT == ACT_BF16 ? 2 : 4;
     const int lb = blockIdx.z;
     const int b = lb % p.B;
     if (p.active && p.active[b] == 0) return;
     const int c0 = (blockIdx.x * CONV_CT + threadIdx.x) * 8;
     if (c0 >= p.C) return;
-    const int t0 = blockIdx.y * CONV_TR;
+    const int t0 = blockIdx.y * TR;
     const int l = lb / p.B;
 
+    // ---- every load first: window rows t0 .. t0 + TR + 2, then weights ----
+    uint4 raw[TR + 3][NV];
+#pragma unroll
+    for (int r = 0; r < TR + 3; ++r) {
+        const int q = min(t0 + r, p.T + 2);   // window row; rows < 3 live in conv_state
+        const char* src = q < 3 ? static_cast<const char*>(p.conv_state) +
+                                      ((static_cast<size_t>(lb) * 3 + q) * p.C + c0) * ESZ
+                                : static_cast<const char*>(p.x) +
+                                      ((static_cast<size_t>(lb) * p.T + (q - 3)) * p.C + c0) * ESZ;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) raw[r][v] = reinterpret_cast<const uint4*>(src)[v];
+    }
     float w[4][8], bias[8];
     {
         // conv_w[l][c][0..3] for 8 channels = 32 contiguous values.
-        float raw[32];
+        float wr[32];
         const size_t wi = (static_cast<size_t>(l) * p.C + c0) * 4;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) load_vec8<ACT>(p.conv_w, wi + 8 * q, raw + 8 * q);
+        for (int q = 0; q < 4; ++q) load_vec8<ACT>(p.conv_w, wi + 8 * q, wr + 8 * q);
 #pragma unroll
         for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[j][c] = raw[c * 4 + j];
+            for (int j = 0; j < 4; ++j) w[j][c] = wr[c * 4 + j];
     }
     if (p.conv_b) {
         load_vec8<ACT>(p.conv_b, static_cast<size_t>(l) * p.C + c0, bias);
@@ -159,22 +196,14 @@ __global__ __launch_bounds__(CONV_CT) void conv_kernel(ConvParams p)
         for (int c = 0; c < 8; ++c) bias[c] = 0.0f;
     }
 
-    // Window rows t0 .. t0+2 (rows < 3 live in conv_state).
+    const bool use_silu = (p.flags & FLAG_SILU) != 0;
     float win[4][8];
 #pragma unroll
-    for (int r = 0; r < 3; ++r) {
-        const int q = t0 + r;
-        if (q < 3)
-            load_vec8<ACT>(p.conv_state, (static_cast<size_t>(lb) * 3 + q) * p.C + c0, win[r]);
-        else
-            load_vec8<ACT>(p.x, (static_cast<size_t>(lb) * p.T + (q - 3)) * p.C + c0, win[r]);
-    }
-    const bool use_silu = (p.flags & FLAG_SILU) != 0;
+    for (int r = 0; r < 3; ++r) to_f32x8<ACT>(raw[r], win[r]);
 #pragma unroll
-    for (int i = 0; i < CONV_TR; ++i) {
+    for (int i = 0; i < TR; ++i) {
         const int t = t0 + i;
-        if (t >= p.T) break;
-        load_vec8<ACT>(p.x, (static_cast<size_t>(lb) * p.T + t) * p.C + c0, win[3]);
+        to_f32x8<ACT>(raw[i + 3], win[3]);
         float yv[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -183,9 +212,9 @@ __global__ __launch_bounds__(CONV_CT) void conv_kernel(ConvParams p)
             acc = fmaf(w[2][c], win[2][c], acc);
             acc = fmaf(w[3][c], win[3][c], acc);
             acc += bias[c];
-            yv[c] = use_silu ? silu(acc) : acc;
+            yv[c] = use_silu ? silu_hw(acc) : acc;
         }
-        store_vec8(p.y, (static_cast<size_t>(lb) * p.T + t) * p.C + c0, p.out, yv);
+        if (t < p.T) store_vec8(p.y, (static_cast<size_t>(lb) * p.T + t) * p.C + c0, p.out, yv);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             win[0][c] = win[1][c];
@@ -193,22 +222,58 @@ __global__ __launch_bounds__(CONV_CT) void conv_kernel(ConvParams p)
             win[2][c] = win[3][c];
         }
     }
+
+    // ---- cache commit: conv_state <- W[T .. T+2] ----
+    // Only the first token tile reads the old cache (TR >= 3), and each of its
+    // threads reads exactly the 8 channels it rewrites, after the loop above
+    // has consumed them.
+    if (p.commit && blockIdx.y == 0) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const int q = p.T + r;   // window row that becomes cache row r
+            uint4 v[NV];
+            if (q < TR + 3) {
+#pragma unroll
+                for (int k = 0; k < TR + 3; ++k)
+                    if (k == q)
+#pragma unroll
+                        for (int u = 0; u < NV; ++u) v[u] = raw[k][u];
+            } else {
+                const uint4* src = reinterpret_cast<const uint4*>(
+                    static_cast<const char*>(p.x) + ((static_cast<size_t>(lb) * p.T + (q - 3)) * p.C + c0) * ESZ);
+#pragma unroll
+                for (int u = 0; u < NV; ++u) v[u] = src[u];
+            }
+            uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(p.conv_state) +
+                                                  ((static_cast<size_t>(lb) * 3 + r) * p.C + c0) * ESZ);
+#pragma unroll
+            for (int u = 0; u < NV; ++u) dst[u] = v[u];
+        }
+    }
 }
 
-hipError_t launch_conv(const ConvParams& p, hipStream_t s)
+template <int TR>
+hipError_t launch_conv_tr(const ConvParams& p, hipStream_t s)
 {
     const int gx = (p.C + 8 * CONV_CT - 1) / (8 * CONV_CT);
-    const int gy = (p.T + CONV_TR - 1) / CONV_TR;
+    const int gy = (p.T + TR - 1) / TR;
     const long long gz = static_cast<long long>(p.L) * p.B;
     if (gy > 65535 || gz > 65535 || gz <= 0) return hipErrorInvalidConfiguration;
     clear_stale_error();
     if (p.act == ACT_BF16)
-        hipLaunchKernelGGL(conv_kernel<ACT_BF16>, dim3(gx, gy, static_cast<unsigned>(gz)), dim3(CONV_CT),
+        hipLaunchKernelGGL((conv_kernel<ACT_BF16, TR>), dim3(gx, gy, static_cast<unsigned>(gz)), dim3(CONV_CT),
                            0, s, p);
     else
-        hipLaunchKernelGGL(conv_kernel<ACT_F32>, dim3(gx, gy, static_cast<unsigned>(gz)), dim3(CONV_CT),
+        hipLaunchKernelGGL((conv_kernel<ACT_F32, TR>), dim3(gx, gy, static_cast<unsigned>(gz)), dim3(CONV_CT),
                            0, s, p);
     return hipGetLastError();
+}
+
+// Short windows (decode) use 4 tokens per thread, long ones (prefill) 8: at
+// 1,024 tokens and 8,192 channels that is 1,024 workgroups of two waves.
+hipError_t launch_conv(const ConvParams& p, hipStream_t s)
+{
+    return p.T <= 8 ? launch_conv_tr<4>(p, s) : launch_conv_tr<8>(p, s);
 }
 
 }  // namespace gdn

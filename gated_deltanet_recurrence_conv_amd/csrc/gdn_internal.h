@@ -41,7 +41,7 @@ struct RecParams {
 
 // ---------------------------------------------------------------------------
 // Conv-window shift (commit, rewind, conv_step with commit_state).
-enum WinMode { WIN_COMMIT = 0, WIN_REWIND = 1, WIN_FULL = 2 };
+enum WinMode { WIN_COMMIT = 0, WIN_REWIND = 1 };
 
 struct WinParams {
     const void* x;
@@ -61,12 +61,13 @@ struct ConvParams {
     const void* x;
     const void* conv_w;
     const void* conv_b;
-    const void* conv_state;
+    void* conv_state;
     void* y;
     const uint8_t* active;
     int32_t L, B, T, C;
     int32_t act, out;
     uint32_t flags;
+    int32_t commit;   // also shift the cache by T tokens
 };
 
 // Drops an error a previous runtime call may have left behind, so that the

@@ -164,11 +164,13 @@ def test_verify_window_matches_prefill():
     assert state_err(sp, st_r[:, :, 4]) <= 2e-3 and out_err(host(o2), o_r) <= 2e-3
 
 
-@pytest.mark.parametrize("T", [1, 7, 1024])
+@pytest.mark.parametrize("T", [1, 3, 7, 37, 1024])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_conv_step_parity(T, out):
     """The short causal conv over T tokens at the Qwen channel count
-    (2*16*128 + 32*128 = 8192), rows 1 and 6 inactive, cache committed."""
+    (2*16*128 + 32*128 = 8192), rows 1 and 6 inactive, cache committed.
+    T = 7 and 37 leave ragged token tiles for both tile heights; the cache
+    commit takes its new rows from registers (T = 1, 3) or from x (T >= 5)."""
     torch = torch_mod()
     sh = W.COHORT.with_(T=T, B=8 if T < 1024 else 2, inactive=(1, 6) if T < 1024 else (1,))
     inp = W.verify_inputs(sh, seed=3500 + T)
