@@ -30,6 +30,8 @@
 // Workgroups are dispatched round-robin over the 8 XCDs; the block index is
 // remapped so that all waves of one (layer, row, qk head) -- which read the
 // same q/k conv channels -- land on the same XCD and share its L2.
+#include <atomic>
+
 #include "gdn_internal.h"
 
 namespace gdn {
@@ -249,22 +251,48 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
     }
 }
 
+// Occupancy cap.  Each wave streams its state slice once; more than one of
+// these waves resident per SIMD only adds concurrent DRAM streams and costs
+// bandwidth (measured at the B8/T2 cohort over 30 layers: one wave per SIMD
+// 5.86 TB/s, two 5.56, three 5.30).  The cap is set by reserving dynamic LDS
+// so that exactly kWgPerCU one-wave workgroups fit in a CU's LDS.
+constexpr int kWgPerCU = 4;   // one wave per SIMD
+
+static size_t occupancy_lds_bytes(size_t static_bytes)
+{
+    static std::atomic<int> cached[64];   // LDS bytes per CU, per device; 0 = not queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int lds = cached[dev].load(std::memory_order_relaxed);
+    if (lds == 0) {
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+            lds <= 0)
+            return 0;
+        cached[dev].store(lds, std::memory_order_relaxed);
+    }
+    // a per-workgroup allocation in (lds / (kWgPerCU + 1), lds / kWgPerCU]
+    const size_t total = static_cast<size_t>(lds) / kWgPerCU - 1024;
+    return total > static_bytes ? total - static_bytes : 0;
+}
+
 template <int DK, int DV>
 static hipError_t launch_rec(RecParams p, hipStream_t s)
 {
     constexpr int SW = DV < 32 ? DV : 32;
     constexpr int NS = DV / SW;
+    constexpr size_t STATIC_LDS = sizeof(float) * 4 * (2 * DK + SW);   // ys[4][NCH]
     p.groups = p.L * p.B * p.HK;
     p.per_group = (p.HV / p.HK) * NS;
     const long long blocks = static_cast<long long>((p.groups + 7) / 8) * 8 * p.per_group;
     if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const size_t dyn = occupancy_lds_bytes(STATIC_LDS);
     clear_stale_error();
     if (p.act == ACT_BF16)
         hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_BF16>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(64), 0, s, p);
+                           dim3(64), dyn, s, p);
     else
         hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_F32>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(64), 0, s, p);
+                           dim3(64), dyn, s, p);
     return hipGetLastError();
 }
 
