@@ -251,15 +251,20 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
     }
 }
 
-// Occupancy cap.  Each wave streams its state slice once; more than one of
-// these waves resident per SIMD only adds concurrent DRAM streams and costs
-// bandwidth (measured at the B8/T2 cohort over 30 layers: one wave per SIMD
-// 5.86 TB/s, two 5.56, three 5.30).  The cap is set by reserving dynamic LDS
-// so that exactly kWgPerCU one-wave workgroups fit in a CU's LDS.
-constexpr int kWgPerCU = 4;   // one wave per SIMD
+// Occupancy cap for verify.  A verify wave streams its state slice in and its
+// candidates out with little arithmetic between; more than one such wave
+// resident per SIMD only adds concurrent DRAM streams and costs bandwidth
+// (measured at the B8/T2 cohort over 30 layers: one wave per SIMD 5.86 TB/s,
+// two 5.56, three 5.30).  The cap is set by reserving dynamic LDS so that
+// exactly wg_per_cu one-wave workgroups fit in a CU's LDS.  Rewind computes
+// up to T steps between its single read and single write of the slice and
+// needs the other waves to cover that, so it runs uncapped.
+constexpr int kVerifyWgPerCU = 4;   // one wave per SIMD
+constexpr int kRewindWgPerCU = 0;   // no cap
 
-static size_t occupancy_lds_bytes(size_t static_bytes)
+static size_t occupancy_lds_bytes(size_t static_bytes, int wg_per_cu)
 {
+    if (wg_per_cu <= 0) return 0;
     static std::atomic<int> cached[64];   // LDS bytes per CU, per device; 0 = not queried
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -270,8 +275,8 @@ static size_t occupancy_lds_bytes(size_t static_bytes)
             return 0;
         cached[dev].store(lds, std::memory_order_relaxed);
     }
-    // a per-workgroup allocation in (lds / (kWgPerCU + 1), lds / kWgPerCU]
-    const size_t total = static_cast<size_t>(lds) / kWgPerCU - 1024;
+    // a per-workgroup allocation in (lds / (wg_per_cu + 1), lds / wg_per_cu]
+    const size_t total = static_cast<size_t>(lds) / wg_per_cu - 1024;
     return total > static_bytes ? total - static_bytes : 0;
 }
 
@@ -285,7 +290,7 @@ static hipError_t launch_rec(RecParams p, hipStream_t s)
     p.per_group = (p.HV / p.HK) * NS;
     const long long blocks = static_cast<long long>((p.groups + 7) / 8) * 8 * p.per_group;
     if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const size_t dyn = occupancy_lds_bytes(STATIC_LDS);
+    const size_t dyn = occupancy_lds_bytes(STATIC_LDS, p.mode == REC_VERIFY ? kVerifyWgPerCU : kRewindWgPerCU);
     clear_stale_error();
     if (p.act == ACT_BF16)
         hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_BF16>), dim3(static_cast<unsigned>(blocks)),
