@@ -75,6 +75,7 @@ _lib.gdn_conv_step.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int, _
 _lib.gdn_verify.argtypes = [_D] + [_vp] * 12
 _lib.gdn_commit.argtypes = [_D] + [_vp] * 7
 _lib.gdn_rewind.argtypes = [_D] + [_vp] * 12
+_lib.gdn_verify_lazy.argtypes = [_D] + [_vp] * 16
 _lib.gdn_prefill_chunked.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                      ctypes.c_size_t, _vp, _vp]
 _lib.gdn_workspace_size.argtypes = [_D, _i32]
@@ -85,10 +86,11 @@ _lib.gdn_version.argtypes = []
 _lib.gdn_version.restype = ctypes.c_char_p
 _lib.gdn_last_hip_error.argtypes = []
 _lib.gdn_last_hip_error.restype = ctypes.c_char_p
-for _n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_prefill_chunked"):
+for _n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
+           "gdn_prefill_chunked"):
     getattr(_lib, _n).restype = ctypes.c_int
 
-EXPORTED = ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_prefill_chunked",
+EXPORTED = ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy", "gdn_prefill_chunked",
             "gdn_workspace_size", "gdn_status_string", "gdn_version", "gdn_last_hip_error")
 
 
@@ -200,6 +202,23 @@ def gdn_rewind(d, x, conv_w, conv_b, conv_state, g, beta, state, cur, keep, o=No
         _arg(cur, "cur", s["cur"], torch.int32, True),
         _arg(keep, "keep", s["rows"], torch.int32), _arg(o, "o", s["o"], O, True),
         _arg(err, "err", s["err"], torch.int32, True), _stream(stream)), "gdn_rewind")
+
+
+def gdn_verify_lazy(d, x_prev, g_prev, beta_prev, keep_prev, x, conv_w, conv_b, conv_state, g,
+                    beta, state, cur, o, active=None, err=None, stream=None):
+    torch, s = _torch(), _shapes(d)
+    A, O = _act_dtype(d.act), _act_dtype(d.out)
+    _check(_lib.gdn_verify_lazy(
+        ctypes.byref(d), _arg(x_prev, "x_prev", s["x"], A, True),
+        _arg(g_prev, "g_prev", s["g"], A, True), _arg(beta_prev, "beta_prev", s["g"], A, True),
+        _arg(keep_prev, "keep_prev", s["rows"], torch.int32, True),
+        _arg(x, "x", s["x"], A), _arg(conv_w, "conv_w", s["conv_w"], A),
+        _arg(conv_b, "conv_b", s["conv_b"], A, True),
+        _arg(conv_state, "conv_state", s["conv_state"], A), _arg(g, "g", s["g"], A),
+        _arg(beta, "beta", s["g"], A), _arg(state, "state", s["state"], torch.float32),
+        _arg(cur, "cur", s["cur"], torch.int32, True), _arg(o, "o", s["o"], O),
+        _arg(active, "active", s["rows"], torch.uint8, True),
+        _arg(err, "err", s["err"], torch.int32, True), _stream(stream)), "gdn_verify_lazy")
 
 
 def gdn_workspace_size(d, chunk=64) -> int:

@@ -193,6 +193,40 @@ size_t gdn_workspace_size(const gdn_dims* d, int32_t chunk)
     return gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, chunk);
 }
 
+gdn_status gdn_verify_lazy(const gdn_dims* d, const void* x_prev, const void* g_prev,
+                           const void* beta_prev, const int32_t* keep_prev, const void* x,
+                           const void* conv_w, const void* conv_b, void* conv_state,
+                           const void* g, const void* beta, float* state, const int32_t* cur,
+                           void* o, const uint8_t* active, int32_t* err, void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    if (d->T > 4) return GDN_E_SHAPE;
+    st = check_ptrs({x, conv_w, conv_state, g, beta, state, o}, {conv_b, x_prev, g_prev, beta_prev},
+                    {cur, keep_prev, err});
+    if (st != GDN_OK) return st;
+    if (keep_prev && (!x_prev || !g_prev || !beta_prev)) return GDN_E_NULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    RecParams p = rec_params(d);
+    p.x = x; p.conv_w = conv_w; p.conv_b = conv_b; p.conv_state = conv_state;
+    p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.active = active;
+    p.keep = keep_prev; p.err = err; p.mode = gdn::REC_LAZY;
+    // without a previous window nothing is replayed; its inputs are never
+    // used but every load of the kernel is unconditional, so point them at x
+    p.x_prev = keep_prev ? x_prev : x;
+    p.g_prev = keep_prev ? g_prev : g;
+    p.beta_prev = keep_prev ? beta_prev : beta;
+    st = from_hip(gdn::launch_recurrent(p, d->DK, d->DV, s));
+    if (st != GDN_OK || !keep_prev) return st;
+    // The conv cache is shifted by a second launch, after every wave has read
+    // the old cache.
+    WinParams w{};
+    w.x = x_prev; w.conv_state = conv_state; w.cur = const_cast<int32_t*>(cur); w.keep = keep_prev;
+    w.active = nullptr; w.err = err; w.L = d->L; w.B = d->B; w.T = d->T; w.S = d->S;
+    w.C = p.C; w.act = d->act; w.mode = gdn::WIN_REWIND;
+    return from_hip(gdn::launch_window(w, s));
+}
+
 gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* y, const void* g, const void* beta,
                                float* state, const int32_t* cur, void* o, int32_t chunk,
                                void* workspace, size_t workspace_bytes, int32_t* err,

@@ -15,10 +15,13 @@ enum { ERR_KEEP = 1, ERR_SLOT = 2, ERR_INACTIVE_KEEP = 4 };
 // ---------------------------------------------------------------------------
 // Recurrent step kernel (verify and rewind share it, so that a rewind is
 // bit-identical to the verify candidate it replaces).
-enum RecMode { REC_VERIFY = 0, REC_REWIND = 1 };
+enum RecMode { REC_VERIFY = 0, REC_REWIND = 1, REC_LAZY = 2 };
 
 struct RecParams {
     const void* x;
+    const void* x_prev;      // lazy mode: the previous window's x, g, beta
+    const void* g_prev;
+    const void* beta_prev;
     const void* conv_w;
     const void* conv_b;
     const void* conv_state;

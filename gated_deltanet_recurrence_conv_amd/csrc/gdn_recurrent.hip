@@ -46,7 +46,23 @@ __device__ __forceinline__ float sum_over_rows(float v)
     return v;
 }
 
-template <int DK, int DV, int ACT>
+// One of four values chosen by a wave-uniform index (clamped to 0..3), so
+// that register arrays are never indexed dynamically.
+__device__ __forceinline__ float pick4(const float (&v)[4], int i)
+{
+    return i <= 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
+// LAZY: the fused commit-then-verify of one decode cycle ("MTP inference:
+// review and commit structure" (eole docs), Functional commits item 2 and
+// Verification and limits: commits replay only the accepted prefix).  The
+// wave replays the previous window's keep tokens from the snapshot, writes
+// the committed state in place, and runs the new window on from there,
+// writing outputs but no candidates.  Its token sequence is
+// Z = [conv cache ; previous x[0..keep) ; new x[0..T)], so the committed conv
+// cache (rows keep..keep+2 of the previous window) is simply rows keep..keep+2
+// of Z and one conv pass covers both windows.
+template <int DK, int DV, int ACT, bool LAZY>
 __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
 {
     constexpr int SW = DV < 32 ? DV : 32;  // columns per wave
@@ -55,9 +71,10 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
     constexpr int IG = 64 / JL;            // row groups per wave
     constexpr int RPL = DK / IG;           // rows held per lane
     constexpr int NCH = 2 * DK + SW;       // conv channels this wave needs
+    constexpr int MAXT = LAZY ? 8 : 4;     // tokens one wave runs
     static_assert(RPL >= 1 && DK % IG == 0, "tile shape");
 
-    __shared__ float ys[4][NCH];
+    __shared__ float ys[MAXT][NCH];
 
     // ---- block -> (layer, row, qk head, value head, slice), XCD-aware ----
     const int bid = blockIdx.x;
@@ -84,7 +101,17 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
     if (p.active) is_active = p.active[b];
     if (p.keep) kp = p.keep[b];
     int nsteps = p.T;
-    if (p.mode == REC_VERIFY) {
+    if constexpr (LAZY) {
+        int e = 0;
+        if (kp < 0 || kp > p.T) e |= ERR_KEEP;
+        if (slot0 < 0 || slot0 >= p.S) e |= ERR_SLOT;
+        if (e) {
+            if (lane == 0 && p.err) atomicOr(p.err, e);
+            return;
+        }
+        if (is_active == 0 && kp == 0) return;
+        nsteps = kp + (is_active ? p.T : 0);
+    } else if (p.mode == REC_VERIFY) {
         if (is_active == 0) return;
         if (slot0 < 0 || slot0 >= p.S) {
             if (lane == 0 && p.err) atomicOr(p.err, ERR_SLOT);
@@ -113,8 +140,9 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
     const bool has_bias = p.conv_b != nullptr;
     const void* bptr = has_bias ? p.conv_b : p.conv_w;
     constexpr int NG = (NCH + 63) / 64;
+    constexpr int NROW = MAXT + 3;   // window rows per channel
     float wv[NG][4];
-    float win[NG][7];
+    float win[NG][NROW];
     float bias[NG];
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
@@ -128,20 +156,48 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
 #pragma unroll
         for (int r = 0; r < 3; ++r)
             win[n][r] = load_act<ACT>(p.conv_state, (srow + r) * C + c);
+        if constexpr (LAZY) {
+            float xp[4], xn[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            win[n][3 + t] = load_act<ACT>(p.x, (xrow + min(t, p.T - 1)) * C + c);
+            for (int t = 0; t < 4; ++t) {
+                xp[t] = load_act<ACT>(p.x_prev, (xrow + min(t, p.T - 1)) * C + c);
+                xn[t] = load_act<ACT>(p.x, (xrow + min(t, p.T - 1)) * C + c);
+            }
+#pragma unroll
+            for (int j = 0; j < MAXT; ++j) win[n][3 + j] = j < kp ? xp[j < 4 ? j : 3] : pick4(xn, j - kp);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                win[n][3 + t] = load_act<ACT>(p.x, (xrow + min(t, p.T - 1)) * C + c);
+        }
         const float bv = load_act<ACT>(bptr, has_bias ? static_cast<size_t>(l) * C + c : 0);
         bias[n] = has_bias ? bv : 0.0f;
     }
     // Gates of every window token (rows past the window re-read the last one).
     const size_t ghead = xrow * p.HV + hv;  // g/beta index of token 0
-    float gate_a[4], gate_b[4];
+    float gate_a[MAXT], gate_b[MAXT];
+    if constexpr (LAZY) {
+        float gp[4], bp[4], gn[4], bn[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const size_t gi = ghead + static_cast<size_t>(min(t, p.T - 1)) * p.HV;
-        gate_a[t] = load_act<ACT>(p.g, gi);
-        gate_b[t] = load_act<ACT>(p.beta, gi);
+        for (int t = 0; t < 4; ++t) {
+            const size_t gi = ghead + static_cast<size_t>(min(t, p.T - 1)) * p.HV;
+            gp[t] = load_act<ACT>(p.g_prev, gi);
+            bp[t] = load_act<ACT>(p.beta_prev, gi);
+            gn[t] = load_act<ACT>(p.g, gi);
+            bn[t] = load_act<ACT>(p.beta, gi);
+        }
+#pragma unroll
+        for (int j = 0; j < MAXT; ++j) {
+            gate_a[j] = j < kp ? gp[j < 4 ? j : 3] : pick4(gn, j - kp);
+            gate_b[j] = j < kp ? bp[j < 4 ? j : 3] : pick4(bn, j - kp);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const size_t gi = ghead + static_cast<size_t>(min(t, p.T - 1)) * p.HV;
+            gate_a[t] = load_act<ACT>(p.g, gi);
+            gate_b[t] = load_act<ACT>(p.beta, gi);
+        }
     }
 
     // ---- the state slice: every load issued before any use ----
@@ -159,7 +215,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
     for (int n = 0; n < NG; ++n) {
         const int ch = lane + 64 * n;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < MAXT; ++t) {
             float acc = wv[n][0] * win[n][t];
             acc = fmaf(wv[n][1], win[n][t + 1], acc);
             acc = fmaf(wv[n][2], win[n][t + 2], acc);
@@ -205,8 +261,19 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
         const float inv_nk = l2 ? 1.0f / sqrtf(sk + p.l2_eps) : 1.0f;
         const float kqn = kq * inv_nk * inv_nq;
         // t is uniform: select the token's gates without dynamic indexing.
-        const float gt = t == 0 ? gate_a[0] : t == 1 ? gate_a[1] : t == 2 ? gate_a[2] : gate_a[3];
-        const float bt = t == 0 ? gate_b[0] : t == 1 ? gate_b[1] : t == 2 ? gate_b[2] : gate_b[3];
+        float gt, bt;
+        if constexpr (LAZY) {
+            gt = gate_a[MAXT - 1];
+            bt = gate_b[MAXT - 1];
+#pragma unroll
+            for (int j = MAXT - 2; j >= 0; --j) {
+                gt = t == j ? gate_a[j] : gt;
+                bt = t == j ? gate_b[j] : bt;
+            }
+        } else {
+            gt = t == 0 ? gate_a[0] : t == 1 ? gate_a[1] : t == 2 ? gate_a[2] : gate_a[3];
+            bt = t == 0 ? gate_b[0] : t == 1 ? gate_b[1] : t == 2 ? gate_b[2] : gate_b[3];
+        }
         const float a = expf(gt);
 
         float u[4], oo[4];
@@ -223,8 +290,16 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
             for (int c = 0; c < 4; ++c) h[r][c] = fmaf(a, h[r][c], kn * u[c]);
         }
 
-        if (p.o && ig == 0) {
-            const size_t oi = ((xrow + t) * p.HV + hv) * DV + col0;
+        const int tout = LAZY ? t - kp : t;   // token of the window o belongs to
+        if (LAZY && t + 1 == kp) {
+            // committed state of the previous window, in place
+            float* dst = st_lb + (static_cast<size_t>(slot0) * p.HV + hv) * tile + col0;
+#pragma unroll
+            for (int r = 0; r < RPL; ++r)
+                __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(dst + (ig + IG * r) * DV));
+        }
+        if (p.o && ig == 0 && tout >= 0) {
+            const size_t oi = ((xrow + tout) * p.HV + hv) * DV + col0;
             if (p.out == ACT_BF16) {
                 uint2 pk;
                 pk.x = f32_to_bf16_bits(oo[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(oo[1])) << 16);
@@ -235,7 +310,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
                 __builtin_nontemporal_store(ov, reinterpret_cast<f4*>(static_cast<float*>(p.o) + oi));
             }
         }
-        if (p.mode == REC_VERIFY) {
+        if (!LAZY && p.mode == REC_VERIFY) {
             const int slot = (slot0 + t + 1) % p.S;
             float* dst = st_lb + (static_cast<size_t>(slot) * p.HV + hv) * tile + col0;
 #pragma unroll
@@ -243,7 +318,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
                 __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(dst + (ig + IG * r) * DV));
         }
     }
-    if (p.mode == REC_REWIND) {
+    if (!LAZY && p.mode == REC_REWIND) {
         float* dst = st_lb + (static_cast<size_t>(slot0) * p.HV + hv) * tile + col0;
 #pragma unroll
         for (int r = 0; r < RPL; ++r)
@@ -261,6 +336,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
 // needs the other waves to cover that, so it runs uncapped.
 constexpr int kVerifyWgPerCU = 4;   // one wave per SIMD
 constexpr int kRewindWgPerCU = 0;   // no cap
+constexpr int kLazyWgPerCU = 0;     // no cap (replay steps between read and write)
 
 static size_t occupancy_lds_bytes(size_t static_bytes, int wg_per_cu)
 {
@@ -285,19 +361,27 @@ static hipError_t launch_rec(RecParams p, hipStream_t s)
 {
     constexpr int SW = DV < 32 ? DV : 32;
     constexpr int NS = DV / SW;
-    constexpr size_t STATIC_LDS = sizeof(float) * 4 * (2 * DK + SW);   // ys[4][NCH]
+    const bool lazy = p.mode == REC_LAZY;
+    const size_t static_lds = sizeof(float) * (lazy ? 8 : 4) * (2 * DK + SW);   // ys[MAXT][NCH]
     p.groups = p.L * p.B * p.HK;
     p.per_group = (p.HV / p.HK) * NS;
     const long long blocks = static_cast<long long>((p.groups + 7) / 8) * 8 * p.per_group;
     if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const size_t dyn = occupancy_lds_bytes(STATIC_LDS, p.mode == REC_VERIFY ? kVerifyWgPerCU : kRewindWgPerCU);
+    const int cap = p.mode == REC_VERIFY ? kVerifyWgPerCU : p.mode == REC_LAZY ? kLazyWgPerCU : kRewindWgPerCU;
+    const size_t dyn = occupancy_lds_bytes(static_lds, cap);
+    const dim3 grid(static_cast<unsigned>(blocks));
     clear_stale_error();
-    if (p.act == ACT_BF16)
-        hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_BF16>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(64), dyn, s, p);
-    else
-        hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_F32>), dim3(static_cast<unsigned>(blocks)),
-                           dim3(64), dyn, s, p);
+    if (lazy) {
+        if (p.act == ACT_BF16)
+            hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_BF16, true>), grid, dim3(64), dyn, s, p);
+        else
+            hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_F32, true>), grid, dim3(64), dyn, s, p);
+    } else {
+        if (p.act == ACT_BF16)
+            hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_BF16, false>), grid, dim3(64), dyn, s, p);
+        else
+            hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_F32, false>), grid, dim3(64), dyn, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -149,6 +149,29 @@ gdn_status gdn_rewind(const gdn_dims* d, const void* x, const void* conv_w,
                       const void* beta, float* state, const int32_t* cur,
                       const int32_t* keep, void* o, int32_t* err, void* stream);
 
+/* One decode cycle with the commit of the previous cycle folded in ([P2]
+ * Functional commits item 2: accepted-prefix state replay; Verification and
+ * limits: partial commits replay only the accepted recurrent prefix).  For
+ * each row with keep_prev >= 1 the first keep_prev tokens of the previous
+ * window (x_prev, g_prev, beta_prev, same dims) are replayed from slot cur
+ * and the result is written back into slot cur in place, and conv_state
+ * becomes rows keep_prev .. keep_prev+KCONV-2 of [conv_state ; x_prev]; then
+ * the new window (x, g, beta) runs on from that state and o[t] is written
+ * for every active row, with no candidate states.  cur is never changed, so
+ * S may be 1.  The result equals gdn_rewind(previous window, keep_prev)
+ * followed by gdn_verify(new window) bit for bit, with one state read and at
+ * most one state write per (row, head).  keep_prev may be NULL (no previous
+ * window, x_prev/g_prev/beta_prev then unused); active governs only the new
+ * window (inactive rows get no outputs; a nonzero keep_prev is still
+ * committed).  The accepted length of this cycle's window is passed as
+ * keep_prev of the next call; a final gdn_rewind flushes the last one.
+ * err: GDN_ERR_KEEP, GDN_ERR_SLOT (the row is then left untouched). */
+gdn_status gdn_verify_lazy(const gdn_dims* d, const void* x_prev, const void* g_prev,
+                           const void* beta_prev, const int32_t* keep_prev, const void* x,
+                           const void* conv_w, const void* conv_b, void* conv_state,
+                           const void* g, const void* beta, float* state, const int32_t* cur,
+                           void* o, const uint8_t* active, int32_t* err, void* stream);
+
 /* Chunked prompt prefill of the same recurrence ([P1] Measurements:
  * 1,024-token layer-major prefill calls; [P2] Verification and limits: the
  * chunk recurrence equals the sequential one up to rounding).  y holds the

@@ -31,8 +31,8 @@ def declared_functions():
 
 def test_header_declares_the_five_calls():
     names = declared_functions()
-    for n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_prefill_chunked",
-              "gdn_workspace_size", "gdn_status_string", "gdn_version"):
+    for n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
+              "gdn_prefill_chunked", "gdn_workspace_size", "gdn_status_string", "gdn_version"):
         assert n in names
 
 
@@ -120,6 +120,34 @@ def test_commit_rewind_conv_prefill_validation(lib):
     lib.gdn_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
     lib.gdn_workspace_size.restype = ctypes.c_size_t
     assert lib.gdn_workspace_size(ctypes.byref(d), 32) == 0
+
+
+def test_verify_lazy_validation(lib):
+    """Host checks of the fused commit + verify: window length, required
+    pointers, a previous window without its inputs, alignment.  Every call
+    fails before any launch."""
+    f = lib.gdn_verify_lazy
+    f.argtypes = [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 16
+
+    def call(d, **over):
+        a = dict(xp=FAKE, gp=FAKE, bp=FAKE, kp=FAKE, x=FAKE, w=FAKE, b=None, cs=FAKE, g=FAKE,
+                 beta=FAKE, st=FAKE, cur=None, o=FAKE, act=None, err=None)
+        a.update(over)
+        return f(ctypes.byref(d), a["xp"], a["gp"], a["bp"], a["kp"], a["x"], a["w"], a["b"],
+                 a["cs"], a["g"], a["beta"], a["st"], a["cur"], a["o"], a["act"], a["err"], None)
+
+    d = good()
+    d.T = 5
+    assert call(d) == 2                       # windows are at most 4 tokens
+    d = good()
+    assert call(d, o=None) == 1               # outputs are required
+    assert call(d, xp=None) == 1              # previous window named by keep_prev but missing
+    assert call(d, bp=None) == 1
+    assert call(d, kp=FAKE + 2) == 4          # int32 arrays: 4-byte alignment
+    assert call(d, xp=FAKE + 8) == 4
+    d.S = 1                                   # no candidate slots needed ...
+    d.T = 0
+    assert call(d, kp=None, xp=None, gp=None, bp=None) == 2   # ... but T >= 1
 
 
 def test_status_strings_and_version(lib):
