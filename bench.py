@@ -502,6 +502,50 @@ def prefill(torch, gb, W, args):
                 hbm_gbs=byts / (call_ms / 1e3) / 1e9, workspace_bytes=ws.numel())
 
 
+def prefill_ragged(torch, gb, W, args):
+    """Eight prompts of unequal length (seeded, 64..1,024 tokens) prefilled in
+    one 1,024-token launch into their own rows of a B8 state (32 value / 16
+    qk heads, d = 128, bf16 in and out); tokens/s counts real prompt tokens."""
+    sh = W.PREFILL.with_(B=8)
+    d = gb.make_dims(1, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=1, act="bf16", out="bf16")
+    rng = np.random.default_rng(1005)
+    lengths = rng.integers(64, sh.T + 1, size=sh.B).astype(np.int32)
+    lengths[0] = sh.T
+    C = sh.C
+    bf = torch.bfloat16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5006)
+    y = torch.randn((1, sh.B, sh.T, C), generator=gen, device="cuda")
+    qk = y[..., :2 * sh.HK * sh.DK].reshape(1, sh.B, sh.T, 2 * sh.HK, sh.DK)
+    qk /= qk.norm(dim=-1, keepdim=True)
+    y = y.to(bf)
+    g = (-torch.nn.functional.softplus(torch.randn((1, sh.B, sh.T, sh.HV), generator=gen,
+                                                   device="cuda"))).to(bf)
+    b = torch.sigmoid(torch.randn((1, sh.B, sh.T, sh.HV), generator=gen, device="cuda")).to(bf)
+    st = torch.zeros((1, sh.B, 1, sh.HV, sh.DK, sh.DV), device="cuda")
+    o = torch.empty((1, sh.B, sh.T, sh.HV, sh.DV), device="cuda", dtype=bf)
+    ws = torch.empty(gb.gdn_workspace_size(d), dtype=torch.uint8, device="cuda")
+    lens = torch.from_numpy(lengths).cuda()
+    for _ in range(3):
+        gb.gdn_prefill_ragged(d, y, g, b, st, None, o, lens, 64, ws)
+    torch.cuda.synchronize()
+    reps = 20
+    tm = Timer(torch)
+    start = tm.ev()
+    for _ in range(reps):
+        gb.gdn_prefill_ragged(d, y, g, b, st, None, o, lens, 64, ws)
+    end = tm.ev()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    ntok = int(lengths.sum())
+    Cc, dd = 64, sh.DK
+    flops = (6 * dd * dd + 5 * Cc * dd + Cc * Cc / 3.0) * ntok * sh.HV
+    del y, g, b, o, ws
+    torch.cuda.empty_cache()
+    return dict(lengths=lengths.tolist(), call_ms=ms, tokens_per_s=ntok / (ms / 1e3),
+                achieved_tflops=flops / (ms / 1e3) / 1e12)
+
+
 def cpu_baseline(W, budget_s=12.0):
     """The oracle as it stands (single-threaded C, float64) on a bounded
     sample of the headline workload: whole verify + commit layer-cycles of
@@ -549,7 +593,8 @@ def main():
         return
     log("bench: %s on %s" % (gb.gdn_version(), torch.cuda.get_device_name(0)))
     sections = {"per_layer_graph": per_layer_graph, "solo": solo, "rewind": rewind,
-                "conv_step": conv_step, "prefill": prefill, "lazy": lazy_cycle}
+                "conv_step": conv_step, "prefill": prefill, "lazy": lazy_cycle,
+                "prefill_ragged": prefill_ragged}
     if args.only:
         print(json.dumps({args.only: sections[args.only](torch, gb, W, args)}), flush=True)
         return
@@ -561,7 +606,8 @@ def main():
         for name, fn in (("lazy_commit_verify_b8_t2", lazy_cycle),
                          ("per_layer_graph_b8_t2", per_layer_graph), ("solo_b1_t3_l30", solo),
                          ("rewind_b8_t4", rewind), ("conv_step_t1024", conv_step),
-                         ("prefill_b1_4096_in_1024_calls", prefill)):
+                         ("prefill_b1_4096_in_1024_calls", prefill),
+                         ("prefill_ragged_b8_up_to_1024", prefill_ragged)):
             log("bench: %s" % name)
             extra[name] = fn(torch, gb, W, args)
             log("bench: %s -> %s" % (name, json.dumps(extra[name])))

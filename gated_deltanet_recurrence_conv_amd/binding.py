@@ -76,6 +76,8 @@ _lib.gdn_verify.argtypes = [_D] + [_vp] * 12
 _lib.gdn_commit.argtypes = [_D] + [_vp] * 7
 _lib.gdn_rewind.argtypes = [_D] + [_vp] * 12
 _lib.gdn_verify_lazy.argtypes = [_D] + [_vp] * 16
+_lib.gdn_prefill_ragged.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                    ctypes.c_size_t, _vp, _vp]
 _lib.gdn_prefill_chunked.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                      ctypes.c_size_t, _vp, _vp]
 _lib.gdn_workspace_size.argtypes = [_D, _i32]
@@ -87,10 +89,11 @@ _lib.gdn_version.restype = ctypes.c_char_p
 _lib.gdn_last_hip_error.argtypes = []
 _lib.gdn_last_hip_error.restype = ctypes.c_char_p
 for _n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
-           "gdn_prefill_chunked"):
+           "gdn_prefill_chunked", "gdn_prefill_ragged"):
     getattr(_lib, _n).restype = ctypes.c_int
 
-EXPORTED = ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy", "gdn_prefill_chunked",
+EXPORTED = ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
+            "gdn_prefill_chunked", "gdn_prefill_ragged",
             "gdn_workspace_size", "gdn_status_string", "gdn_version", "gdn_last_hip_error")
 
 
@@ -225,25 +228,44 @@ def gdn_workspace_size(d, chunk=64) -> int:
     return int(_lib.gdn_workspace_size(ctypes.byref(d), int(chunk)))
 
 
+def _workspace(d, chunk, workspace):
+    need = gdn_workspace_size(d, chunk)
+    if workspace is None:
+        return None, 0
+    if isinstance(workspace, int):
+        raise TypeError("workspace must be a tensor so that its size is known")
+    ptr = _arg(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError("workspace holds %d bytes, %d needed" % (nbytes, need))
+    return ptr, nbytes
+
+
 def gdn_prefill_chunked(d, y, g, beta, state, cur, o, chunk=64, workspace=None, err=None,
                         stream=None):
     torch, s = _torch(), _shapes(d)
     A, O = _act_dtype(d.act), _act_dtype(d.out)
-    need = gdn_workspace_size(d, chunk)
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        if isinstance(workspace, int):
-            raise TypeError("workspace must be a tensor so that its size is known")
-        ws_ptr = _arg(workspace, "workspace")
-        ws_bytes = workspace.numel() * workspace.element_size()
-        if ws_bytes < need:
-            raise ValueError("workspace holds %d bytes, %d needed" % (ws_bytes, need))
+    ws_ptr, ws_bytes = _workspace(d, chunk, workspace)
     _check(_lib.gdn_prefill_chunked(
         ctypes.byref(d), _arg(y, "y", s["x"], A), _arg(g, "g", s["g"], A),
         _arg(beta, "beta", s["g"], A), _arg(state, "state", s["state"], torch.float32),
         _arg(cur, "cur", s["cur"], torch.int32, True), _arg(o, "o", s["o"], O), int(chunk),
         ws_ptr, ws_bytes, _arg(err, "err", s["err"], torch.int32, True), _stream(stream)),
         "gdn_prefill_chunked")
+
+
+def gdn_prefill_ragged(d, y, g, beta, state, cur, o, lengths, chunk=64, workspace=None, err=None,
+                       stream=None):
+    torch, s = _torch(), _shapes(d)
+    A, O = _act_dtype(d.act), _act_dtype(d.out)
+    ws_ptr, ws_bytes = _workspace(d, chunk, workspace)
+    _check(_lib.gdn_prefill_ragged(
+        ctypes.byref(d), _arg(y, "y", s["x"], A), _arg(g, "g", s["g"], A),
+        _arg(beta, "beta", s["g"], A), _arg(state, "state", s["state"], torch.float32),
+        _arg(cur, "cur", s["cur"], torch.int32, True), _arg(o, "o", s["o"], O),
+        _arg(lengths, "lengths", s["rows"], torch.int32), int(chunk),
+        ws_ptr, ws_bytes, _arg(err, "err", s["err"], torch.int32, True), _stream(stream)),
+        "gdn_prefill_ragged")
 
 
 def gdn_status_string(status: int) -> str:

@@ -227,27 +227,35 @@ gdn_status gdn_verify_lazy(const gdn_dims* d, const void* x_prev, const void* g_
     return from_hip(gdn::launch_window(w, s));
 }
 
+gdn_status gdn_prefill_ragged(const gdn_dims* d, const void* y, const void* g, const void* beta,
+                              float* state, const int32_t* cur, void* o, const int32_t* lengths,
+                              int32_t chunk, void* workspace, size_t workspace_bytes, int32_t* err,
+                              void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    if (chunk != 64) return GDN_E_SHAPE;
+    st = check_ptrs({y, g, beta, state, o}, {workspace}, {cur, lengths, err});
+    if (st != GDN_OK) return st;
+    if (!gdn::prefill_supported(d->DK, d->DV, d->act)) return GDN_E_UNSUPPORTED;
+    const size_t need = gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, chunk);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
+    gdn::PrefillParams p{};
+    p.y = y; p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.ws = workspace;
+    p.err = err; p.lengths = lengths;
+    p.L = d->L; p.B = d->B; p.T = d->T; p.HV = d->HV; p.HK = d->HK; p.S = d->S;
+    p.C = channels(d); p.act = d->act; p.out = d->out;
+    p.scale = d->scale; p.l2_eps = d->l2_eps; p.flags = d->flags;
+    return from_hip(gdn::launch_prefill(p, d->DK, d->DV, static_cast<hipStream_t>(stream)));
+}
+
 gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* y, const void* g, const void* beta,
                                float* state, const int32_t* cur, void* o, int32_t chunk,
                                void* workspace, size_t workspace_bytes, int32_t* err,
                                void* stream)
 {
-    gdn_status st = check_dims(d);
-    if (st != GDN_OK) return st;
-    if (chunk != 64) return GDN_E_SHAPE;
-    st = check_ptrs({y, g, beta, state, o}, {workspace}, {cur, err});
-    if (st != GDN_OK) return st;
-    if (!gdn::prefill_supported(d->DK, d->DV, d->act)) return GDN_E_UNSUPPORTED;
-    if (st != GDN_OK) return st;
-    const size_t need = gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, chunk);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
-    gdn::PrefillParams p{};
-    p.y = y; p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.ws = workspace;
-    p.err = err;
-    p.L = d->L; p.B = d->B; p.T = d->T; p.HV = d->HV; p.HK = d->HK; p.S = d->S;
-    p.C = channels(d); p.act = d->act; p.out = d->out;
-    p.scale = d->scale; p.l2_eps = d->l2_eps; p.flags = d->flags;
-    return from_hip(gdn::launch_prefill(p, d->DK, d->DV, static_cast<hipStream_t>(stream)));
+    return gdn_prefill_ragged(d, y, g, beta, state, cur, o, nullptr, chunk, workspace, workspace_bytes, err,
+                              stream);
 }
 
 }  // extern "C"

@@ -10,7 +10,7 @@ namespace gdn {
 
 enum { ACT_F32 = 0, ACT_BF16 = 1 };
 enum { FLAG_SILU = 1u, FLAG_L2 = 2u };
-enum { ERR_KEEP = 1, ERR_SLOT = 2, ERR_INACTIVE_KEEP = 4 };
+enum { ERR_KEEP = 1, ERR_SLOT = 2, ERR_INACTIVE_KEEP = 4, ERR_LENGTH = 8 };
 
 // ---------------------------------------------------------------------------
 // Recurrent step kernel (verify and rewind share it, so that a rewind is
@@ -91,6 +91,7 @@ struct PrefillParams {
     void* o;
     void* ws;
     int32_t* err;
+    const int32_t* lengths;   // per-row prompt length (ragged), or null: all T
     int32_t L, B, T, HV, HK, S, C;
     int32_t act, out;
     float scale, l2_eps;

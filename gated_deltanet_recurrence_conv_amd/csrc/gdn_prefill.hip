@@ -175,9 +175,12 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
     const int c = blockIdx.x;
     const int hv = blockIdx.y;
     const int lb = blockIdx.z;
-    const int NC = (p.T + CH - 1) / CH;
+    const int NC = (p.T + CH - 1) / CH;   // record layout: the padded length
     const int t0 = c * CH;
-    const int n = min(CH, p.T - t0);
+    const int len = p.lengths ? p.lengths[lb % p.B] : p.T;
+    if (len < 0 || len > p.T) return;     // reported by the scan kernel
+    const int n = min(CH, len - t0);
+    if (n <= 0) return;                   // past this row's prompt
     const int m = hv / (p.HV / p.HK);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -699,12 +702,13 @@ struct ChunkRes {
 };
 
 template <int DK, int DV, int OUT>
-__device__ __forceinline__ ChunkRes chunk_res(const PrefillParams& p, const char* recs, int c, int lb, int hv)
+__device__ __forceinline__ ChunkRes chunk_res(const PrefillParams& p, const char* recs, int c, int len, int lb,
+                                              int hv)
 {
     using R = Rec<DK, DV>;
     constexpr int OSZ = OUT == ACT_BF16 ? 2 : 4;
     const int t0 = c * CH;
-    const int n = min(CH, p.T - t0);
+    const int n = min(CH, len - t0);   // >= 1: c is a chunk of this row's prompt
     ChunkRes r;
     r.rec = make_rsrc(recs + static_cast<size_t>(c) * R::BYTES, static_cast<uint32_t>(R::BYTES));
     const size_t row0 = static_cast<size_t>(lb) * p.T + t0;
@@ -714,8 +718,8 @@ __device__ __forceinline__ ChunkRes chunk_res(const PrefillParams& p, const char
 }
 
 template <int DK, int DV, int OUT, int TA, int TB>
-__device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK>& ring, const char* recs, int NC, int lb,
-                                         int hv, int cs, int lane)
+__device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK>& ring, const char* recs, int NC, int len,
+                                         int lb, int hv, int cs, int lane)
 {
     constexpr int OSZ = OUT == ACT_BF16 ? 2 : 4;
     const int fr = lane & 15, gq = lane >> 4;
@@ -728,16 +732,16 @@ __device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK>& ring,
         for (int j = 0; j < 4; ++j) vo[i][j] = ((16 * tb + 4 * gq + j) * p.HV * DV + 16 * cs + fr) * OSZ;
     }
     OutFrags<DK, DV> fa, fb;
-    ChunkRes ra = chunk_res<DK, DV, OUT>(p, recs, 0, lb, hv), rb;
+    ChunkRes ra = chunk_res<DK, DV, OUT>(p, recs, 0, len, lb, hv), rb;
     out_load<DK, DV, TA, TB>(fa, ra.rec, lane16, vq16);
     int c = 0;
     for (; c + 2 <= NC; c += 2) {
-        rb = chunk_res<DK, DV, OUT>(p, recs, c + 1, lb, hv);
+        rb = chunk_res<DK, DV, OUT>(p, recs, c + 1, len, lb, hv);
         out_load<DK, DV, TA, TB>(fb, rb.rec, lane16, vq16);
         __syncthreads();
         out_chunk<DK, DV, OUT, TA, TB>(fa, ring, c, ra.o, vo, lane);
         const int c2 = min(c + 2, NC - 1);
-        ra = chunk_res<DK, DV, OUT>(p, recs, c2, lb, hv);
+        ra = chunk_res<DK, DV, OUT>(p, recs, c2, len, lb, hv);
         out_load<DK, DV, TA, TB>(fa, ra.rec, lane16, vq16);
         __syncthreads();
         out_chunk<DK, DV, OUT, TA, TB>(fb, ring, c + 1, rb.o, vo, lane);
@@ -776,11 +780,17 @@ __global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform role
 
     const int slot = p.cur ? p.cur[lb] : 0;
-    if (slot < 0 || slot >= p.S) {
-        if (threadIdx.x == 0 && cs == 0 && p.err) atomicOr(p.err, ERR_SLOT);
-        return;
+    const int len = p.lengths ? p.lengths[lb % p.B] : p.T;
+    {
+        const int e = (slot < 0 || slot >= p.S ? ERR_SLOT : 0) | (len < 0 || len > p.T ? ERR_LENGTH : 0);
+        if (e) {
+            if (threadIdx.x == 0 && cs == 0 && hv == m * gsz && p.err) atomicOr(p.err, e);
+            return;
+        }
     }
+    if (len == 0) return;
     const char* recs = static_cast<const char*>(p.ws) + (static_cast<size_t>(lb) * p.HV + hv) * NC * R::BYTES;
+    const int NCr = (len + CH - 1) / CH;   // chunks of this row's prompt
 
     if (w == 0) {
         // ---- state wave ----
@@ -794,14 +804,14 @@ __global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
 #pragma unroll
             for (int j = 0; j < 4; ++j) h[a][j] = st[(16 * a + fq + j) * DV + col];
         auto rec_rsrc = [&](int cc) {
-            return make_rsrc(recs + static_cast<size_t>(min(cc, NC - 1)) * R::BYTES, static_cast<uint32_t>(R::BYTES));
+            return make_rsrc(recs + static_cast<size_t>(min(cc, NCr - 1)) * R::BYTES, static_cast<uint32_t>(R::BYTES));
         };
         WFrags<DK> wf;
         KFrags<DK, DV> fa, fb;
         w_load<DK, DV>(wf, rec_rsrc(0), lane16);
         k_load<DK, DV>(fa, rec_rsrc(0), lane16, vq16, cs);
         int c = 0;
-        for (; c + 2 <= NC; c += 2) {
+        for (; c + 2 <= NCr; c += 2) {
             k_load<DK, DV>(fb, rec_rsrc(c + 1), lane16, vq16, cs);
             state_chunk<DK, DV>(wf, fa, rec_rsrc(c + 1), h, ring, c, lane);
             __syncthreads();
@@ -809,7 +819,7 @@ __global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
             state_chunk<DK, DV>(wf, fb, rec_rsrc(c + 2), h, ring, c + 1, lane);
             __syncthreads();
         }
-        if (c < NC) {
+        if (c < NCr) {
             state_chunk<DK, DV>(wf, fa, rec_rsrc(c), h, ring, c, lane);
             __syncthreads();
         }
@@ -818,9 +828,9 @@ __global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
 #pragma unroll
             for (int j = 0; j < 4; ++j) st[(16 * a + fq + j) * DV + col] = h[a][j];
     } else if (w == 1) {
-        out_wave<DK, DV, OUT, 0, 3>(p, ring, recs, NC, lb, hv, cs, lane);
+        out_wave<DK, DV, OUT, 0, 3>(p, ring, recs, NCr, len, lb, hv, cs, lane);
     } else {
-        out_wave<DK, DV, OUT, 1, 2>(p, ring, recs, NC, lb, hv, cs, lane);
+        out_wave<DK, DV, OUT, 1, 2>(p, ring, recs, NCr, len, lb, hv, cs, lane);
     }
 }
 

@@ -88,6 +88,7 @@ typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
 #define GDN_ERR_KEEP 1          /* keep[b] outside 0..T */
 #define GDN_ERR_SLOT 2          /* cur[l][b] outside 0..S-1 */
 #define GDN_ERR_INACTIVE_KEEP 4 /* keep[b] != 0 on an inactive row */
+#define GDN_ERR_LENGTH 8        /* lengths[b] outside 0..T (ragged prefill) */
 
 typedef struct {
     int32_t L, B, T;        /* layers, rows, tokens per call */
@@ -186,6 +187,22 @@ gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* y, const void* g,
                                const void* beta, float* state, const int32_t* cur, void* o,
                                int32_t chunk, void* workspace, size_t workspace_bytes,
                                int32_t* err, void* stream);
+
+/* Ragged multi-prompt prefill ([P3] What was broken items 1 and 5: several
+ * prompts of unequal length prefilled into the rows of one row-owned B8
+ * state): gdn_prefill_chunked where row b holds a prompt of lengths[b]
+ * tokens (device int32 [B], the same for every layer, 0 <= lengths[b] <= T).
+ * y, g, beta and o keep the padded [L][B][T][...] layout with T the longest
+ * prompt; the tokens of row b past lengths[b] are never read, their o rows
+ * are never written, and the state of slot cur is advanced over exactly
+ * lengths[b] tokens (a row of length 0 is left untouched).  Row b's result
+ * equals gdn_prefill_chunked on that row alone with T = lengths[b] bit for
+ * bit.  workspace: gdn_workspace_size(d, chunk) bytes as for the padded call.
+ * err: GDN_ERR_SLOT, GDN_ERR_LENGTH (the row is then left untouched). */
+gdn_status gdn_prefill_ragged(const gdn_dims* d, const void* y, const void* g, const void* beta,
+                              float* state, const int32_t* cur, void* o, const int32_t* lengths,
+                              int32_t chunk, void* workspace, size_t workspace_bytes,
+                              int32_t* err, void* stream);
 
 /* Workspace bytes gdn_prefill_chunked needs for these dims (0 on bad dims). */
 size_t gdn_workspace_size(const gdn_dims* d, int32_t chunk);

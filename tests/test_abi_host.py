@@ -117,6 +117,12 @@ def test_commit_rewind_conv_prefill_validation(lib):
         [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     assert lib.gdn_prefill_chunked(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, 32,
                                    None, 0, None, None) == 2    # chunk must be 64
+    lib.gdn_prefill_ragged.argtypes = [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 7 + \
+        [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.gdn_prefill_ragged(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE + 2,
+                                  64, FAKE, 1 << 40, None, None) == 4   # lengths misaligned
+    assert lib.gdn_prefill_ragged(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                  64, FAKE, 16, None, None) == 6        # workspace too small
     lib.gdn_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
     lib.gdn_workspace_size.restype = ctypes.c_size_t
     assert lib.gdn_workspace_size(ctypes.byref(d), 32) == 0

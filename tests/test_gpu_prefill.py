@@ -205,3 +205,72 @@ def test_prefill_rejects_unsupported_and_small_workspace():
     with pytest.raises(B().GdnError) as ei:
         B().gdn_prefill_chunked(d, z, gg, gg, st, None, o, 64, torch.zeros(1 << 20, dtype=torch.uint8, device="cuda"))
     assert ei.value.status == 5   # d_k = 16 is not supported by the chunked kernels
+
+
+def test_prefill_ragged_rows_equal_single_row_calls():
+    """Eight prompts of unequal length (0 .. 1,000 tokens) in one launch into
+    their own rows ("Add request-owned eight-way MTP serving for Qwen 35B",
+    What was broken items 1 and 5): each row equals a single-row call of its
+    own length bit for bit and the token-sequential oracle within 2e-3; a
+    row of length 0 and the padding past every prompt are untouched."""
+    torch = torch_mod()
+    lengths = np.array([0, 1, 63, 64, 65, 200, 1000, 13], np.int32)
+    T = int(lengths.max())
+    sh = W.Shape("pfr", L=1, B=8, T=T, HV=4, HK=2, DK=128, DV=64, S=2)
+    inp = W.prefill_inputs(sh, seed=3600)
+    inp["state"] = W.random_state(sh, seed=3601)
+    inp["cur"] = np.array([[0, 1, 1, 0, 1, 0, 0, 1]], np.int32)
+    A = act_dtype(sh.act)
+    d, _ = dims_pair(sh)
+    st = dev(inp["state"], torch.float32)
+    o = torch.full((1, sh.B, T, sh.HV, sh.DV), float("nan"), device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(B().gdn_workspace_size(d), dtype=torch.uint8, device="cuda")
+    B().gdn_prefill_ragged(d, dev(inp["y"], A), dev(inp["g"], A), dev(inp["beta"], A), st,
+                           dev(inp["cur"], torch.int32), o, dev(lengths), 64, ws, err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    st_g, o_g = host(st), host(o)
+    for b, n in enumerate(lengths):
+        c0 = int(inp["cur"][0, b])
+        others = [s for s in range(sh.S) if s != c0]
+        assert np.array_equal(st_g[:, b, others], inp["state"][:, b, others])
+        assert np.all(np.isnan(o_g[:, b, n:]))
+        if n == 0:
+            assert np.array_equal(st_g[:, b], inp["state"][:, b])
+            continue
+        one = sh.with_(B=1, T=int(n))
+        row = {k: np.ascontiguousarray(inp[k][:, b:b + 1, :n]) for k in ("y", "g", "beta")}
+        row["state"] = np.ascontiguousarray(inp["state"][:, b:b + 1])
+        row["cur"] = np.ascontiguousarray(inp["cur"][:, b:b + 1])
+        st1, o1 = gpu_prefill(one, row)
+        assert np.array_equal(st_g[:, b:b + 1], st1)
+        assert np.array_equal(o_g[:, b:b + 1, :n], o1)
+        st_r, o_r, e = oracle_prefill(one, row)
+        assert e == 0
+        assert state_err(st_g[:, b:b + 1, c0], st_r[:, :, c0]) <= 2e-3
+        assert out_err(o_g[:, b:b + 1, :n], o_r) <= 2e-3
+
+
+def test_prefill_ragged_bad_length_reported():
+    torch = torch_mod()
+    sh = W.Shape("pfe", L=1, B=3, T=100, HV=2, HK=1, DK=64, DV=32, S=1)
+    inp = W.prefill_inputs(sh, seed=3700)
+    inp["state"] = W.random_state(sh, seed=3701)
+    A = act_dtype(sh.act)
+    d, _ = dims_pair(sh)
+    st = dev(inp["state"], torch.float32)
+    o = torch.full((1, sh.B, sh.T, sh.HV, sh.DV), float("nan"), device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(B().gdn_workspace_size(d), dtype=torch.uint8, device="cuda")
+    lengths = np.array([50, sh.T + 1, -1], np.int32)
+    B().gdn_prefill_ragged(d, dev(inp["y"], A), dev(inp["g"], A), dev(inp["beta"], A), st, None,
+                           o, dev(lengths), 64, ws, err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 8
+    st_g, o_g = host(st), host(o)
+    for b in (1, 2):
+        assert np.array_equal(st_g[:, b], inp["state"][:, b])
+        assert np.all(np.isnan(o_g[:, b]))
+    assert not np.array_equal(st_g[:, 0], inp["state"][:, 0])
+    assert np.all(np.isfinite(o_g[:, 0, :50])) and np.all(np.isnan(o_g[:, 0, 50:]))
