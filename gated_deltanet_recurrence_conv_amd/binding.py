@@ -76,6 +76,7 @@ _lib.gdn_verify.argtypes = [_D] + [_vp] * 12
 _lib.gdn_commit.argtypes = [_D] + [_vp] * 7
 _lib.gdn_rewind.argtypes = [_D] + [_vp] * 12
 _lib.gdn_verify_lazy.argtypes = [_D] + [_vp] * 16
+_lib.gdn_accept_greedy.argtypes = [_D] + [_vp] * 6
 _lib.gdn_prefill_ragged.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                     ctypes.c_size_t, _vp, _vp]
 _lib.gdn_prefill_chunked.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
@@ -89,11 +90,11 @@ _lib.gdn_version.restype = ctypes.c_char_p
 _lib.gdn_last_hip_error.argtypes = []
 _lib.gdn_last_hip_error.restype = ctypes.c_char_p
 for _n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
-           "gdn_prefill_chunked", "gdn_prefill_ragged"):
+           "gdn_accept_greedy", "gdn_prefill_chunked", "gdn_prefill_ragged"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
-            "gdn_prefill_chunked", "gdn_prefill_ragged",
+            "gdn_accept_greedy", "gdn_prefill_chunked", "gdn_prefill_ragged",
             "gdn_workspace_size", "gdn_status_string", "gdn_version", "gdn_last_hip_error")
 
 
@@ -226,6 +227,16 @@ def gdn_verify_lazy(d, x_prev, g_prev, beta_prev, keep_prev, x, conv_w, conv_b, 
 
 def gdn_workspace_size(d, chunk=64) -> int:
     return int(_lib.gdn_workspace_size(ctypes.byref(d), int(chunk)))
+
+
+def gdn_accept_greedy(d, draft_ids, target_ids, keep, active=None, next_ids=None, stream=None):
+    torch = _torch()
+    B, T = d.B, d.T
+    _check(_lib.gdn_accept_greedy(
+        ctypes.byref(d), _arg(draft_ids, "draft_ids", (B, T - 1), torch.int32, True) if T > 1 else None,
+        _arg(target_ids, "target_ids", (B, T), torch.int32), _arg(active, "active", (B,), torch.uint8, True),
+        _arg(keep, "keep", (B,), torch.int32), _arg(next_ids, "next_ids", (B,), torch.int32, True),
+        _stream(stream)), "gdn_accept_greedy")
 
 
 def _workspace(d, chunk, workspace):

@@ -227,6 +227,22 @@ gdn_status gdn_verify_lazy(const gdn_dims* d, const void* x_prev, const void* g_
     return from_hip(gdn::launch_window(w, s));
 }
 
+gdn_status gdn_accept_greedy(const gdn_dims* d, const int32_t* draft_ids, const int32_t* target_ids,
+                             const uint8_t* active, int32_t* keep, int32_t* next_ids, void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    if (d->T > 4) return GDN_E_SHAPE;
+    if (!target_ids || !keep || (d->T > 1 && !draft_ids)) return GDN_E_NULL;
+    st = check_ptrs({}, {}, {draft_ids, target_ids, keep, next_ids});
+    if (st != GDN_OK) return st;
+    gdn::AcceptParams p{};
+    p.draft = d->T > 1 ? draft_ids : nullptr;
+    p.target = target_ids; p.active = active; p.keep = keep; p.next = next_ids;
+    p.B = d->B; p.T = d->T;
+    return from_hip(gdn::launch_accept(p, static_cast<hipStream_t>(stream)));
+}
+
 gdn_status gdn_prefill_ragged(const gdn_dims* d, const void* y, const void* g, const void* beta,
                               float* state, const int32_t* cur, void* o, const int32_t* lengths,
                               int32_t chunk, void* workspace, size_t workspace_bytes, int32_t* err,

@@ -97,6 +97,17 @@ struct PrefillParams {
     float scale, l2_eps;
     uint32_t flags;
 };
+// Greedy acceptance of a verification window.
+struct AcceptParams {
+    const int32_t* draft;    // [B][T-1] (null when T == 1)
+    const int32_t* target;   // [B][T]
+    const uint8_t* active;   // [B] or null
+    int32_t* keep;           // [B]
+    int32_t* next;           // [B] or null
+    int32_t B, T;
+};
+hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
+
 bool prefill_supported(int DK, int DV, int act);
 size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int chunk);
 hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s);

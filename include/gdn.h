@@ -173,6 +173,23 @@ gdn_status gdn_verify_lazy(const gdn_dims* d, const void* x_prev, const void* g_
                            const void* g, const void* beta, float* state, const int32_t* cur,
                            void* o, const uint8_t* active, int32_t* err, void* stream);
 
+/* Greedy acceptance of the verified window on the device ([P3] Follow-up:
+ * the greedy cohort route keeps the draft IDs on the device and transfers only
+ * token-ID arrays; What was broken item 2: keep in {0, 1, 2} at T = 2).
+ * Window token 0 is the pending token, tokens 1..T-1 are the drafts
+ * draft_ids [B][T-1] (may be NULL when T = 1); target_ids [B][T] holds the
+ * target model's greedy token after each window position (its argmax, taken
+ * by the caller).  For active rows keep[b] = 1 + the number of leading drafts
+ * with draft_ids[b][j] == target_ids[b][j] (the first mismatch ends the
+ * prefix), and next_ids[b] (optional) = target_ids[b][keep[b] - 1], the next
+ * pending token; inactive rows get keep[b] = 0 and no next token.  All arrays
+ * are device int32 (active uint8); keep can go straight into gdn_commit or
+ * gdn_verify_lazy on the same stream.  Only d->B and d->T are used (the dims
+ * are still validated as for gdn_verify). */
+gdn_status gdn_accept_greedy(const gdn_dims* d, const int32_t* draft_ids, const int32_t* target_ids,
+                             const uint8_t* active, int32_t* keep, int32_t* next_ids,
+                             void* stream);
+
 /* Chunked prompt prefill of the same recurrence ([P1] Measurements:
  * 1,024-token layer-major prefill calls; [P2] Verification and limits: the
  * chunk recurrence equals the sequential one up to rounding).  y holds the

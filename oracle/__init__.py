@@ -87,6 +87,8 @@ def _bind(lib):
     lib.ora_rewind.restype = ip
     lib.ora_prefill.argtypes = [ctypes.POINTER(_Dims)] + [vp] * 6
     lib.ora_prefill.restype = ip
+    lib.ora_accept_greedy.argtypes = [ctypes.POINTER(_Dims)] + [vp] * 5
+    lib.ora_accept_greedy.restype = None
     return lib
 
 
@@ -189,6 +191,19 @@ def commit(d: Dims, x, conv_state, cur, keep, active=None):
     act = _u8(active, s["active"])
     err = _load().ora_commit(ctypes.byref(d._c()), _p(x_), _p(cs), _p(cu), _p(kp), _p(act))
     return cs, cu, err
+
+
+def accept_greedy(d: Dims, draft, target, active=None, next_init=None):
+    """draft [B][T-1], target [B][T] int32 token ids.  Returns (keep, next);
+    next holds next_init (default -1) where nothing is written."""
+    B, T = d.B, d.T
+    dr = np.ascontiguousarray(np.asarray(draft, np.int32).reshape(B, max(T - 1, 0)))
+    tg = np.ascontiguousarray(np.asarray(target, np.int32).reshape(B, T))
+    act = None if active is None else np.ascontiguousarray(np.asarray(active, np.uint8).reshape(B))
+    keep = np.zeros(B, np.int32)
+    nxt = np.full(B, -1, np.int32) if next_init is None else np.array(next_init, np.int32).reshape(B)
+    _load().ora_accept_greedy(ctypes.byref(d._c()), _p(dr), _p(tg), _p(act), _p(keep), _p(nxt))
+    return keep, nxt
 
 
 def rewind(d: Dims, x, conv_w, conv_b, conv_state, g, beta, state, cur, keep, o_init=None,

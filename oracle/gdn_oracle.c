@@ -293,3 +293,31 @@ int ora_prefill(const ora_dims* d, const double* y, const double* g, const doubl
         }
     return err;
 }
+
+/*
+ * Greedy acceptance of a verification window ("Add request-owned eight-way
+ * MTP serving for Qwen 35B", Follow-up: the greedy cohort route keeps the
+ * draft IDs on the device and transfers only token-ID arrays; What was broken
+ * item 2: a row commits two tokens, one token, or none).  Window token 0 is
+ * the already-sampled pending token, tokens 1..T-1 are drafts; target[b][j]
+ * is the target model's greedy token after window position j.  A draft is
+ * accepted while it equals the target's token at the position before it, so
+ * keep = 1 + the number of leading drafts that match, and the next pending
+ * token is the target's token after the last kept position.  Inactive rows
+ * get keep = 0 and no next token.
+ */
+void ora_accept_greedy(const ora_dims* d, const int32_t* draft, const int32_t* target,
+                       const uint8_t* active, int32_t* keep, int32_t* next)
+{
+    const int T = d->T;
+    for (int b = 0; b < d->B; ++b) {
+        if (active && !active[b]) {
+            keep[b] = 0;
+            continue;
+        }
+        int k = 1;
+        while (k < T && draft[(size_t)b * (T - 1) + (k - 1)] == target[(size_t)b * T + (k - 1)]) k++;
+        keep[b] = k;
+        if (next) next[b] = target[(size_t)b * T + (k - 1)];
+    }
+}

@@ -394,4 +394,30 @@ def pin_error_bits(ora):
     assert np.array_equal(st, inp["state"].astype(np.float64))
 
 
+def pin_greedy_acceptance(ora):
+    """Greedy acceptance of a window ("Add request-owned eight-way MTP serving
+    for Qwen 35B", Follow-up; What was broken item 2): keep counts the pending
+    token plus the leading drafts that equal the target's token one position
+    earlier; the first mismatch ends the prefix (later matches do not count);
+    an inactive row keeps 0; the next pending token is the target's token
+    after the last kept position.  Every case below is written out by hand."""
+    d = ora.Dims(L=1, B=7, T=4, HV=2, HK=1, DK=16, DV=16, S=5)
+    target = np.array([[10, 11, 12, 13]] * 7, np.int32)
+    draft = np.array([[10, 11, 12],     # all accepted
+                      [99, 11, 12],     # first draft rejected
+                      [10, 99, 12],     # second rejected
+                      [10, 11, 99],     # third rejected
+                      [99, 11, 12],     # later matches after a mismatch do not count
+                      [11, 12, 13],     # drafts shifted by one: compared position by position
+                      [10, 11, 12]], np.int32)
+    active = np.array([1, 1, 1, 1, 1, 1, 0], np.uint8)
+    keep, nxt = ora.accept_greedy(d, draft, target, active)
+    assert keep.tolist() == [4, 1, 2, 3, 1, 1, 0]
+    assert nxt.tolist() == [13, 10, 11, 12, 10, 10, -1]
+    # T = 1: no drafts, the pending token alone
+    d1 = ora.Dims(L=1, B=2, T=1, HV=2, HK=1, DK=16, DV=16, S=2)
+    keep, nxt = ora.accept_greedy(d1, np.zeros((2, 0), np.int32), np.array([[5], [6]], np.int32))
+    assert keep.tolist() == [1, 1] and nxt.tolist() == [5, 6]
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

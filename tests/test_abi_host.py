@@ -156,6 +156,18 @@ def test_verify_lazy_validation(lib):
     assert call(d, kp=None, xp=None, gp=None, bp=None) == 2   # ... but T >= 1
 
 
+def test_accept_greedy_validation(lib):
+    f = lib.gdn_accept_greedy
+    f.argtypes = [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 6
+    d = good()
+    assert f(ctypes.byref(d), None, FAKE, None, FAKE, None, None) == 1    # drafts needed at T = 2
+    assert f(ctypes.byref(d), FAKE, None, None, FAKE, None, None) == 1    # targets needed
+    assert f(ctypes.byref(d), FAKE, FAKE, None, None, None, None) == 1    # keep needed
+    assert f(ctypes.byref(d), FAKE, FAKE, None, FAKE + 2, None, None) == 4
+    d.T = 5
+    assert f(ctypes.byref(d), FAKE, FAKE, None, FAKE, None, None) == 2
+
+
 def test_status_strings_and_version(lib):
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_version.restype = ctypes.c_char_p

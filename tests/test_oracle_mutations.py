@@ -44,6 +44,10 @@ MUTANTS = {
     "verify_ignores_active": ("if (!row_active(active, b)) continue;\n            int c0 = cur ? cur[l * d->B + b] : 0;\n            if (c0 < 0 || c0 >= d->S) { err |= 2; continue; }\n            memcpy(h,",
                               "int c0 = cur ? cur[l * d->B + b] : 0;\n            if (c0 < 0 || c0 >= d->S) { err |= 2; continue; }\n            memcpy(h,"),
     "rewind_one_token_short": ("for (int t = 0; t < kp; ++t) {", "for (int t = 0; t + 1 < kp; ++t) {"),
+    "accept_compares_same_position": ("== target[(size_t)b * T + (k - 1)]) k++;",
+                                      "== target[(size_t)b * T + k]) k++;"),
+    "accept_next_one_late": ("if (next) next[b] = target[(size_t)b * T + (k - 1)];",
+                             "if (next) next[b] = target[(size_t)b * T + (k < T ? k : k - 1)];"),
 }
 
 
