@@ -546,6 +546,49 @@ def prefill_ragged(torch, gb, W, args):
                 achieved_tflops=flops / (ms / 1e3) / 1e12)
 
 
+def gated_rmsnorm(torch, gb, W, args):
+    """The gated RMSNorm epilogue over the cohort's verify outputs (30 layers x
+    8 rows x 2 tokens x 32 heads x 128, fp32 o, bf16 gate and weight, written
+    in place), 10 launches captured in one HIP graph."""
+    sh = W.COHORT
+    d = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
+                     out="f32")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5007)
+    shp = (L_POOL, sh.B, sh.T, sh.HV, sh.DV)
+    o = torch.randn(shp, generator=gen, device="cuda")
+    z = torch.randn(shp, generator=gen, device="cuda").to(torch.bfloat16)
+    w = (1.0 + 0.1 * torch.randn((L_POOL, sh.DV), generator=gen, device="cuda")).to(torch.bfloat16)
+    act_rows = np.ones(sh.B, np.uint8)
+    for r in sh.inactive:
+        act_rows[r] = 0
+    active = torch.from_numpy(act_rows).cuda()
+    gb.gdn_gated_rmsnorm(d, o, z, w, o, active=active)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    n = 10
+    with torch.cuda.graph(graph, stream=s):
+        for _ in range(n):
+            gb.gdn_gated_rmsnorm(d, o, z, w, o, active=active)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    start = tm.ev()
+    for _ in range(5):
+        graph.replay()
+    end = tm.ev()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / (5 * n)
+    na = int(act_rows.sum())
+    byts = L_POOL * na * sh.T * sh.HV * sh.DV * (4 + 2 + 4) + L_POOL * sh.DV * 2
+    del o, z, graph
+    torch.cuda.empty_cache()
+    return dict(ms_per_call=ms, bytes_per_call=byts, gbs=byts / (ms / 1e3) / 1e9)
+
+
 def cpu_baseline(W, budget_s=12.0):
     """The oracle as it stands (single-threaded C, float64) on a bounded
     sample of the headline workload: whole verify + commit layer-cycles of
@@ -594,7 +637,7 @@ def main():
     log("bench: %s on %s" % (gb.gdn_version(), torch.cuda.get_device_name(0)))
     sections = {"per_layer_graph": per_layer_graph, "solo": solo, "rewind": rewind,
                 "conv_step": conv_step, "prefill": prefill, "lazy": lazy_cycle,
-                "prefill_ragged": prefill_ragged}
+                "prefill_ragged": prefill_ragged, "gated_rmsnorm": gated_rmsnorm}
     if args.only:
         print(json.dumps({args.only: sections[args.only](torch, gb, W, args)}), flush=True)
         return
@@ -607,7 +650,8 @@ def main():
                          ("per_layer_graph_b8_t2", per_layer_graph), ("solo_b1_t3_l30", solo),
                          ("rewind_b8_t4", rewind), ("conv_step_t1024", conv_step),
                          ("prefill_b1_4096_in_1024_calls", prefill),
-                         ("prefill_ragged_b8_up_to_1024", prefill_ragged)):
+                         ("prefill_ragged_b8_up_to_1024", prefill_ragged),
+                         ("gated_rmsnorm_b8_t2_l30", gated_rmsnorm)):
             log("bench: %s" % name)
             extra[name] = fn(torch, gb, W, args)
             log("bench: %s -> %s" % (name, json.dumps(extra[name])))

@@ -77,6 +77,7 @@ _lib.gdn_commit.argtypes = [_D] + [_vp] * 7
 _lib.gdn_rewind.argtypes = [_D] + [_vp] * 12
 _lib.gdn_verify_lazy.argtypes = [_D] + [_vp] * 16
 _lib.gdn_accept_greedy.argtypes = [_D] + [_vp] * 6
+_lib.gdn_gated_rmsnorm.argtypes = [_D, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp]
 _lib.gdn_prefill_ragged.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                     ctypes.c_size_t, _vp, _vp]
 _lib.gdn_prefill_chunked.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
@@ -90,11 +91,11 @@ _lib.gdn_version.restype = ctypes.c_char_p
 _lib.gdn_last_hip_error.argtypes = []
 _lib.gdn_last_hip_error.restype = ctypes.c_char_p
 for _n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
-           "gdn_accept_greedy", "gdn_prefill_chunked", "gdn_prefill_ragged"):
+           "gdn_accept_greedy", "gdn_gated_rmsnorm", "gdn_prefill_chunked", "gdn_prefill_ragged"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
-            "gdn_accept_greedy", "gdn_prefill_chunked", "gdn_prefill_ragged",
+            "gdn_accept_greedy", "gdn_gated_rmsnorm", "gdn_prefill_chunked", "gdn_prefill_ragged",
             "gdn_workspace_size", "gdn_status_string", "gdn_version", "gdn_last_hip_error")
 
 
@@ -237,6 +238,16 @@ def gdn_accept_greedy(d, draft_ids, target_ids, keep, active=None, next_ids=None
         _arg(target_ids, "target_ids", (B, T), torch.int32), _arg(active, "active", (B,), torch.uint8, True),
         _arg(keep, "keep", (B,), torch.int32), _arg(next_ids, "next_ids", (B,), torch.int32, True),
         _stream(stream)), "gdn_accept_greedy")
+
+
+def gdn_gated_rmsnorm(d, o, z, w, y, eps=1e-6, active=None, stream=None):
+    s = _shapes(d)
+    A, O = _act_dtype(d.act), _act_dtype(d.out)
+    _check(_lib.gdn_gated_rmsnorm(
+        ctypes.byref(d), _arg(o, "o", s["o"], O), _arg(z, "z", s["o"], A),
+        _arg(w, "w", (d.L, d.DV), A), float(eps), _arg(y, "y", s["o"], O),
+        _arg(active, "active", s["rows"], _torch().uint8, True), _stream(stream)),
+        "gdn_gated_rmsnorm")
 
 
 def _workspace(d, chunk, workspace):

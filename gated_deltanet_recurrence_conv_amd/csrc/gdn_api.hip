@@ -243,6 +243,21 @@ gdn_status gdn_accept_greedy(const gdn_dims* d, const int32_t* draft_ids, const 
     return from_hip(gdn::launch_accept(p, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_gated_rmsnorm(const gdn_dims* d, const void* o, const void* z, const void* w,
+                             float eps, void* y, const uint8_t* active, void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    if (!(eps >= 0.0f)) return GDN_E_SHAPE;
+    st = check_ptrs({o, z, w, y}, {}, {});
+    if (st != GDN_OK) return st;
+    gdn::NormParams p{};
+    p.o = o; p.z = z; p.w = w; p.y = y; p.active = active;
+    p.L = d->L; p.B = d->B; p.T = d->T; p.HV = d->HV; p.DV = d->DV;
+    p.act = d->act; p.out = d->out; p.eps = eps;
+    return from_hip(gdn::launch_gated_rmsnorm(p, static_cast<hipStream_t>(stream)));
+}
+
 gdn_status gdn_prefill_ragged(const gdn_dims* d, const void* y, const void* g, const void* beta,
                               float* state, const int32_t* cur, void* o, const int32_t* lengths,
                               int32_t chunk, void* workspace, size_t workspace_bytes, int32_t* err,

@@ -108,6 +108,19 @@ struct AcceptParams {
 };
 hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
 
+// Gated RMSNorm epilogue.
+struct NormParams {
+    const void* o;        // [L][B][T][HV][DV], out dtype
+    const void* z;        // same shape, act dtype
+    const void* w;        // [L][DV], act dtype
+    void* y;              // like o (may alias it)
+    const uint8_t* active;
+    int32_t L, B, T, HV, DV;
+    int32_t act, out;
+    float eps;
+};
+hipError_t launch_gated_rmsnorm(const NormParams& p, hipStream_t s);
+
 bool prefill_supported(int DK, int DV, int act);
 size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int chunk);
 hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s);

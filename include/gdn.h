@@ -190,6 +190,16 @@ gdn_status gdn_accept_greedy(const gdn_dims* d, const int32_t* draft_ids, const 
                              const uint8_t* active, int32_t* keep, int32_t* next_ids,
                              void* stream);
 
+/* Gated RMSNorm epilogue of the mixer output ([P2] Functional commits item 4:
+ * the gated RMSNorm of the FLA path): for every (layer, row, token, value
+ * head), y[j] = o[j] / sqrt(mean_j(o^2) + eps) * w[l][j] * SiLU(z[j]).
+ * o and y: [L][B][T][HV][DV] in the out dtype (y may alias o); z: same shape
+ * in the act dtype; w: [L][DV] in the act dtype.  Inactive rows (active NULL
+ * => all active) are not written.  Works after gdn_verify, gdn_verify_lazy,
+ * gdn_rewind (T = keep window) and the prefills (T = prompt tokens). */
+gdn_status gdn_gated_rmsnorm(const gdn_dims* d, const void* o, const void* z, const void* w,
+                             float eps, void* y, const uint8_t* active, void* stream);
+
 /* Chunked prompt prefill of the same recurrence ([P1] Measurements:
  * 1,024-token layer-major prefill calls; [P2] Verification and limits: the
  * chunk recurrence equals the sequential one up to rounding).  y holds the

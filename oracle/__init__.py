@@ -89,6 +89,8 @@ def _bind(lib):
     lib.ora_prefill.restype = ip
     lib.ora_accept_greedy.argtypes = [ctypes.POINTER(_Dims)] + [vp] * 5
     lib.ora_accept_greedy.restype = None
+    lib.ora_gated_rmsnorm.argtypes = [ctypes.POINTER(_Dims), vp, vp, vp, ctypes.c_double, vp, vp]
+    lib.ora_gated_rmsnorm.restype = None
     return lib
 
 
@@ -204,6 +206,18 @@ def accept_greedy(d: Dims, draft, target, active=None, next_init=None):
     nxt = np.full(B, -1, np.int32) if next_init is None else np.array(next_init, np.int32).reshape(B)
     _load().ora_accept_greedy(ctypes.byref(d._c()), _p(dr), _p(tg), _p(act), _p(keep), _p(nxt))
     return keep, nxt
+
+
+def gated_rmsnorm(d: Dims, o, z, w, eps=1e-6, active=None, y_init=None):
+    """o, z [L][B][T][HV][DV]; w [L][DV].  Returns y (y_init where not written)."""
+    s = _shapes(d)
+    o_ = _f64(o, s["o"])
+    z_ = _f64(z, s["o"])
+    w_ = _f64(w, (d.L, d.DV))
+    act = None if active is None else np.ascontiguousarray(np.asarray(active, np.uint8).reshape(d.B))
+    y = _f64(y_init, s["o"]) if y_init is not None else np.zeros(s["o"], np.float64)
+    _load().ora_gated_rmsnorm(ctypes.byref(d._c()), _p(o_), _p(z_), _p(w_), float(eps), _p(act), _p(y))
+    return y
 
 
 def rewind(d: Dims, x, conv_w, conv_b, conv_state, g, beta, state, cur, keep, o_init=None,

@@ -321,3 +321,33 @@ void ora_accept_greedy(const ora_dims* d, const int32_t* draft, const int32_t* t
         if (next) next[b] = target[(size_t)b * T + (k - 1)];
     }
 }
+
+/*
+ * Gated RMSNorm epilogue ("MTP inference: review and commit structure" (eole
+ * docs), Functional commits item 4: the gated RMSNorm that follows the mixer
+ * in the FLA kernels).  The pages name it only; the reading is the usual
+ * one: for every (layer, row, token, value head) the d_v outputs are divided
+ * by their root mean square, then scaled per column by the layer's weight and
+ * by SiLU of the gate z:  y = o / sqrt(mean(o^2) + eps) * w * z / (1 + e^-z).
+ * Inactive rows are skipped (y is not written).
+ */
+void ora_gated_rmsnorm(const ora_dims* d, const double* o, const double* z, const double* w,
+                       double eps, const uint8_t* active, double* y)
+{
+    const int DV = d->DV;
+    for (int l = 0; l < d->L; ++l)
+        for (int b = 0; b < d->B; ++b) {
+            if (active && !active[b]) continue;
+            for (int t = 0; t < d->T; ++t)
+                for (int h = 0; h < d->HV; ++h) {
+                    const size_t base = ((((size_t)l * d->B + b) * d->T + t) * d->HV + h) * DV;
+                    double ss = 0.0;
+                    for (int j = 0; j < DV; ++j) ss += o[base + j] * o[base + j];
+                    const double r = 1.0 / sqrt(ss / DV + eps);
+                    for (int j = 0; j < DV; ++j) {
+                        const double zz = z[base + j];
+                        y[base + j] = o[base + j] * r * w[(size_t)l * DV + j] * (zz / (1.0 + exp(-zz)));
+                    }
+                }
+        }
+}

@@ -420,4 +420,38 @@ def pin_greedy_acceptance(ora):
     assert keep.tolist() == [1, 1] and nxt.tolist() == [5, 6]
 
 
+def pin_gated_rmsnorm(ora):
+    """Gated RMSNorm epilogue ("MTP inference: review and commit structure",
+    Functional commits item 4) pinned by properties of its definition:
+    invariance to a positive scale of o (eps = 0), oddness in o, unit mean
+    square when w = 1 and the gate is saturated (SiLU(60) = 60 in double),
+    a zero gate gives zero, SiLU(z) - SiLU(-z) = z, a one-hot weight keeps one
+    column, the constant-vector closed form, inactive rows untouched."""
+    rng = np.random.default_rng(171)
+    d = ora.Dims(L=2, B=3, T=2, HV=3, HK=1, DK=16, DV=16, S=3)
+    shp = (2, 3, 2, 3, 16)
+    o = rng.standard_normal(shp)
+    z = rng.standard_normal(shp)
+    w = rng.standard_normal((2, 16))
+    y = ora.gated_rmsnorm(d, o, z, w, eps=0.0)
+    assert np.allclose(ora.gated_rmsnorm(d, 7.5 * o, z, w, eps=0.0), y, rtol=1e-13, atol=0)
+    assert np.array_equal(ora.gated_rmsnorm(d, -o, z, w, eps=1e-6), -ora.gated_rmsnorm(d, o, z, w, eps=1e-6))
+    unit = ora.gated_rmsnorm(d, o, np.full(shp, 60.0), np.ones((2, 16)), eps=0.0) / 60.0
+    assert np.allclose(np.mean(unit ** 2, axis=-1), 1.0, rtol=0, atol=1e-13)
+    assert np.array_equal(ora.gated_rmsnorm(d, o, np.zeros(shp), w), np.zeros(shp))
+    yp, ym = ora.gated_rmsnorm(d, o, z, w, eps=0.0), ora.gated_rmsnorm(d, o, -z, w, eps=0.0)
+    base = ora.gated_rmsnorm(d, o, np.full(shp, 60.0), w, eps=0.0) / 60.0   # o / rms(o) * w
+    assert np.allclose(yp - ym, base * z, rtol=1e-12, atol=1e-13)
+    onehot = np.zeros((2, 16))
+    onehot[:, 5] = 1.0
+    y1 = ora.gated_rmsnorm(d, o, z, onehot)
+    assert np.count_nonzero(y1[..., np.arange(16) != 5]) == 0 and np.all(y1[..., 5] != 0)
+    c = np.full(shp, 0.25)
+    yc = ora.gated_rmsnorm(d, c, np.full(shp, 60.0), np.ones((2, 16)), eps=0.0625)
+    assert np.allclose(yc, 0.25 / np.sqrt(0.0625 + 0.0625) * 60.0, rtol=1e-15, atol=0)
+    sentinel = np.full(shp, np.nan)
+    ya = ora.gated_rmsnorm(d, o, z, w, active=np.array([1, 0, 1], np.uint8), y_init=sentinel)
+    assert np.all(np.isnan(ya[:, 1])) and np.all(np.isfinite(ya[:, [0, 2]]))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -168,6 +168,18 @@ def test_accept_greedy_validation(lib):
     assert f(ctypes.byref(d), FAKE, FAKE, None, FAKE, None, None) == 2
 
 
+def test_gated_rmsnorm_validation(lib):
+    f = lib.gdn_gated_rmsnorm
+    f.argtypes = [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    d = good()
+    assert f(ctypes.byref(d), FAKE, None, FAKE, 1e-6, FAKE, None, None) == 1   # z missing
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE + 2, 1e-6, FAKE, None, None) == 4
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, -1.0, FAKE, None, None) == 2   # eps < 0
+    d.DV = 12
+    assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 1e-6, FAKE, None, None) == 2
+
+
 def test_status_strings_and_version(lib):
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_version.restype = ctypes.c_char_p

@@ -46,6 +46,10 @@ MUTANTS = {
     "rewind_one_token_short": ("for (int t = 0; t < kp; ++t) {", "for (int t = 0; t + 1 < kp; ++t) {"),
     "accept_compares_same_position": ("== target[(size_t)b * T + (k - 1)]) k++;",
                                       "== target[(size_t)b * T + k]) k++;"),
+    "rmsnorm_sum_not_mean": ("const double r = 1.0 / sqrt(ss / DV + eps);",
+                             "const double r = 1.0 / sqrt(ss + eps);"),
+    "rmsnorm_gate_without_silu": ("* (zz / (1.0 + exp(-zz)));", "* zz;"),
+    "rmsnorm_weight_by_head": ("w[(size_t)l * DV + j]", "w[(size_t)l * DV + (h % DV)]"),
     "accept_next_one_late": ("if (next) next[b] = target[(size_t)b * T + (k - 1)];",
                              "if (next) next[b] = target[(size_t)b * T + (k < T ? k : k - 1)];"),
 }
