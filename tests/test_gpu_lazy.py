@@ -221,3 +221,74 @@ def test_lazy_error_bits_leave_rows_untouched():
         assert np.array_equal(host(r.state)[:, b], snap[:, b])
         assert np.array_equal(host(r.cs)[:, b], cs0[:, b])
         assert np.all(np.isnan(o[:, b]))
+
+
+def test_device_resident_decode_loop_in_a_graph():
+    """A decode loop that never leaves the device, as the greedy cohort route
+    of "Add request-owned eight-way MTP serving for Qwen 35B" (Follow-up)
+    runs it: each cycle commits the previous window and verifies the new one
+    (gdn_verify_lazy), then accepts greedily (gdn_accept_greedy) into the keep
+    the next cycle commits.  Six cycles captured in one HIP graph and replayed
+    from the same start state equal the same calls made eagerly, bit for bit,
+    on every replay."""
+    torch = torch_mod()
+    sh = W.COHORT.with_(L=2, S=1)
+    ncyc = 6
+    A = act_dtype(sh.act)
+    bd, _ = dims_pair(sh)
+    wins = [W.verify_inputs(sh, seed=5700 + c) for c in range(ncyc)]
+    rng = np.random.default_rng(5799)
+    xs = [dev(wn["x"], A) for wn in wins]
+    gs = [dev(wn["g"], A) for wn in wins]
+    bs = [dev(wn["beta"], A) for wn in wins]
+    targets, drafts = [], []
+    for _ in range(ncyc):
+        t = rng.integers(0, 151_000, size=(sh.B, sh.T)).astype(np.int32)
+        dr = t[:, :sh.T - 1].copy()
+        miss = rng.random(dr.shape) > 0.7
+        dr[miss] += 1
+        targets.append(dev(t))
+        drafts.append(dev(dr))
+    act = dev(wins[0]["active"], torch.uint8)
+    w = dev(wins[0]["conv_w"], A)
+    cs0 = dev(wins[0]["conv_state"], A)
+    st0 = dev(wins[0]["state"], torch.float32)
+
+    def fresh():
+        return dict(cs=cs0.clone(), st=st0.clone(),
+                    keep=torch.zeros(sh.B, dtype=torch.int32, device="cuda"),
+                    nxt=torch.zeros(sh.B, dtype=torch.int32, device="cuda"),
+                    o=torch.zeros((ncyc,) + (sh.L, sh.B, sh.T, sh.HV, sh.DV), device="cuda"),
+                    err=torch.zeros(1, dtype=torch.int32, device="cuda"))
+
+    def loop(r):
+        for c in range(ncyc):
+            prev = c > 0
+            B().gdn_verify_lazy(bd, xs[c - 1] if prev else None, gs[c - 1] if prev else None,
+                                bs[c - 1] if prev else None, r["keep"] if prev else None, xs[c], w,
+                                None, r["cs"], gs[c], bs[c], r["st"], None, r["o"][c], act,
+                                r["err"])
+            B().gdn_accept_greedy(bd, drafts[c], targets[c], r["keep"], act, r["nxt"])
+
+    eager = fresh()
+    loop(eager)
+    torch.cuda.synchronize()
+    assert int(host(eager["err"])[0]) == 0
+    g = fresh()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        loop(g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        g["cs"].copy_(cs0)
+        g["st"].copy_(st0)
+        g["keep"].zero_()
+        g["o"].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ("cs", "st", "keep", "nxt", "o"):
+            assert np.array_equal(host(g[k]), host(eager[k])), (rep, k)
+        assert int(host(g["err"])[0]) == 0
