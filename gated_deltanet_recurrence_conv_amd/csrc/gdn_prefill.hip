@@ -182,6 +182,9 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
     const int n = min(CH, len - t0);
     if (n <= 0) return;                   // past this row's prompt
     const int m = hv / (p.HV / p.HK);
+    // the raw K and Q fragments are the same for every value head of qk head
+    // m: only its first value head stores them
+    const bool kq_owner = hv % (p.HV / p.HK) == 0;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
@@ -246,8 +249,10 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
         for (int ks = 0; ks < KS; ++ks) qf[ks] = make_uint4(0, 0, 0, 0);
     char* rec = static_cast<char*>(p.ws) + ((static_cast<size_t>(lb) * p.HV + hv) * NC + c) * R::BYTES;
     // raw Q rows of token tile w: the A operand of the output products
+    if (kq_owner)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<uint4*>(rec + R::QA + ((w * KS + ks) * 64 + lane) * 16) = qf[ks];
+        for (int ks = 0; ks < KS; ++ks)
+            *reinterpret_cast<uint4*>(rec + R::QA + ((w * KS + ks) * 64 + lane) * 16) = qf[ks];
     float sq = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
             for (int ks = 0; ks < 2; ++ks) {
                 const uint4 f = frag_from_c(d4[2 * ks], d4[2 * ks + 1]);
                 KTf[db][ks][lane] = f;
-                *reinterpret_cast<uint4*>(rec + R::KT + ((db * 2 + ks) * 64 + lane) * 16) = f;
+                if (kq_owner) *reinterpret_cast<uint4*>(rec + R::KT + ((db * 2 + ks) * 64 + lane) * 16) = f;
             }
         }
         for (int nt = w; nt < DV / 16; nt += 4) {
@@ -351,8 +356,10 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
         for (int ks = 0; ks < 2; ++ks) {
             uint4 h, l;
             split8(pv[ks], h, l);
-            *reinterpret_cast<uint4*>(rec + R::PH + ((w * 2 + ks) * 64 + lane) * 16) = h;
-            *reinterpret_cast<uint4*>(rec + R::PL + ((w * 2 + ks) * 64 + lane) * 16) = l;
+            if (w >= 2 || ks == 0) {   // tiles 0 and 1 see only the first 32 tokens
+                *reinterpret_cast<uint4*>(rec + R::PH + ((w * 2 + ks) * 64 + lane) * 16) = h;
+                *reinterpret_cast<uint4*>(rec + R::PL + ((w * 2 + ks) * 64 + lane) * 16) = l;
+            }
         }
         float* vec = reinterpret_cast<float*>(rec + R::VEC);
         if (gq == 0) vec[r_me] = (r_me < n) ? p.scale * exp2f(g_me) * inq_me : 0.f;
@@ -548,7 +555,7 @@ __device__ __forceinline__ void w_load(WFrags<DK>& f, rsrc_t r, int lane16)
 }
 
 template <int DK, int DV>
-__device__ __forceinline__ void k_load(KFrags<DK, DV>& f, rsrc_t r, int lane16, int vq16, int cs)
+__device__ __forceinline__ void k_load(KFrags<DK, DV>& f, rsrc_t r, rsrc_t rk, int lane16, int vq16, int cs)
 {
     using R = Rec<DK, DV>;
 #pragma unroll
@@ -559,7 +566,7 @@ __device__ __forceinline__ void k_load(KFrags<DK, DV>& f, rsrc_t r, int lane16, 
 #pragma unroll
     for (int a = 0; a < DK / 16; ++a)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) f.kt[a][ks] = bload16(r, lane16, R::KT + (a * 2 + ks) * 1024);
+        for (int ks = 0; ks < 2; ++ks) f.kt[a][ks] = bload16(rk, lane16, R::KT + (a * 2 + ks) * 1024);
     f.gC = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 0, R::VEC + 2 * CH * 4, 0));
 }
 
@@ -630,14 +637,14 @@ struct OutFrags {
 };
 
 template <int DK, int DV, int TA, int TB>
-__device__ __forceinline__ void out_load(OutFrags<DK, DV>& f, rsrc_t rrec, int lane16, int vq16)
+__device__ __forceinline__ void out_load(OutFrags<DK, DV>& f, rsrc_t rrec, rsrc_t rq, int lane16, int vq16)
 {
     using R = Rec<DK, DV>;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int tb = i ? TB : TA;
 #pragma unroll
-        for (int ks = 0; ks < R::KS; ++ks) f.q[i][ks] = bload16(rrec, lane16, R::QA + (tb * R::KS + ks) * 1024);
+        for (int ks = 0; ks < R::KS; ++ks) f.q[i][ks] = bload16(rq, lane16, R::QA + (tb * R::KS + ks) * 1024);
 #pragma unroll
         for (int ks = 0; ks < pu_steps(tb); ++ks) {
             f.ph[i][ks] = bload16(rrec, lane16, R::PH + (tb * 2 + ks) * 1024);
@@ -698,12 +705,12 @@ __device__ __forceinline__ void out_chunk(const OutFrags<DK, DV>& f, const Ring<
 
 // resources of chunk c: its workspace record and its output rows
 struct ChunkRes {
-    rsrc_t rec, o;
+    rsrc_t rec, kq, o;   // own record, the qk head's K/Q fragments, output rows
 };
 
 template <int DK, int DV, int OUT>
-__device__ __forceinline__ ChunkRes chunk_res(const PrefillParams& p, const char* recs, int c, int len, int lb,
-                                              int hv)
+__device__ __forceinline__ ChunkRes chunk_res(const PrefillParams& p, const char* recs, const char* recs_kq, int c,
+                                              int len, int lb, int hv)
 {
     using R = Rec<DK, DV>;
     constexpr int OSZ = OUT == ACT_BF16 ? 2 : 4;
@@ -711,6 +718,7 @@ __device__ __forceinline__ ChunkRes chunk_res(const PrefillParams& p, const char
     const int n = min(CH, len - t0);   // >= 1: c is a chunk of this row's prompt
     ChunkRes r;
     r.rec = make_rsrc(recs + static_cast<size_t>(c) * R::BYTES, static_cast<uint32_t>(R::BYTES));
+    r.kq = make_rsrc(recs_kq + static_cast<size_t>(c) * R::BYTES, static_cast<uint32_t>(R::BYTES));
     const size_t row0 = static_cast<size_t>(lb) * p.T + t0;
     r.o = make_rsrc(static_cast<const char*>(p.o) + ((row0 * p.HV + hv) * DV) * OSZ,
                     static_cast<uint32_t>(((n - 1) * p.HV + 1) * DV * OSZ));
@@ -718,8 +726,8 @@ __device__ __forceinline__ ChunkRes chunk_res(const PrefillParams& p, const char
 }
 
 template <int DK, int DV, int OUT, int TA, int TB>
-__device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK>& ring, const char* recs, int NC, int len,
-                                         int lb, int hv, int cs, int lane)
+__device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK>& ring, const char* recs, const char* recs_kq,
+                                         int NC, int len, int lb, int hv, int cs, int lane)
 {
     constexpr int OSZ = OUT == ACT_BF16 ? 2 : 4;
     const int fr = lane & 15, gq = lane >> 4;
@@ -732,17 +740,17 @@ __device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK>& ring,
         for (int j = 0; j < 4; ++j) vo[i][j] = ((16 * tb + 4 * gq + j) * p.HV * DV + 16 * cs + fr) * OSZ;
     }
     OutFrags<DK, DV> fa, fb;
-    ChunkRes ra = chunk_res<DK, DV, OUT>(p, recs, 0, len, lb, hv), rb;
-    out_load<DK, DV, TA, TB>(fa, ra.rec, lane16, vq16);
+    ChunkRes ra = chunk_res<DK, DV, OUT>(p, recs, recs_kq, 0, len, lb, hv), rb;
+    out_load<DK, DV, TA, TB>(fa, ra.rec, ra.kq, lane16, vq16);
     int c = 0;
     for (; c + 2 <= NC; c += 2) {
-        rb = chunk_res<DK, DV, OUT>(p, recs, c + 1, len, lb, hv);
-        out_load<DK, DV, TA, TB>(fb, rb.rec, lane16, vq16);
+        rb = chunk_res<DK, DV, OUT>(p, recs, recs_kq, c + 1, len, lb, hv);
+        out_load<DK, DV, TA, TB>(fb, rb.rec, rb.kq, lane16, vq16);
         __syncthreads();
         out_chunk<DK, DV, OUT, TA, TB>(fa, ring, c, ra.o, vo, lane);
         const int c2 = min(c + 2, NC - 1);
-        ra = chunk_res<DK, DV, OUT>(p, recs, c2, len, lb, hv);
-        out_load<DK, DV, TA, TB>(fa, ra.rec, lane16, vq16);
+        ra = chunk_res<DK, DV, OUT>(p, recs, recs_kq, c2, len, lb, hv);
+        out_load<DK, DV, TA, TB>(fa, ra.rec, ra.kq, lane16, vq16);
         __syncthreads();
         out_chunk<DK, DV, OUT, TA, TB>(fb, ring, c + 1, rb.o, vo, lane);
     }
@@ -790,6 +798,8 @@ __global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
     }
     if (len == 0) return;
     const char* recs = static_cast<const char*>(p.ws) + (static_cast<size_t>(lb) * p.HV + hv) * NC * R::BYTES;
+    // K^T and Q fragments live in the records of the qk head's first value head
+    const char* recs_kq = static_cast<const char*>(p.ws) + (static_cast<size_t>(lb) * p.HV + m * gsz) * NC * R::BYTES;
     const int NCr = (len + CH - 1) / CH;   // chunks of this row's prompt
 
     if (w == 0) {
@@ -806,16 +816,20 @@ __global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
         auto rec_rsrc = [&](int cc) {
             return make_rsrc(recs + static_cast<size_t>(min(cc, NCr - 1)) * R::BYTES, static_cast<uint32_t>(R::BYTES));
         };
+        auto kq_rsrc = [&](int cc) {
+            return make_rsrc(recs_kq + static_cast<size_t>(min(cc, NCr - 1)) * R::BYTES,
+                             static_cast<uint32_t>(R::BYTES));
+        };
         WFrags<DK> wf;
         KFrags<DK, DV> fa, fb;
         w_load<DK, DV>(wf, rec_rsrc(0), lane16);
-        k_load<DK, DV>(fa, rec_rsrc(0), lane16, vq16, cs);
+        k_load<DK, DV>(fa, rec_rsrc(0), kq_rsrc(0), lane16, vq16, cs);
         int c = 0;
         for (; c + 2 <= NCr; c += 2) {
-            k_load<DK, DV>(fb, rec_rsrc(c + 1), lane16, vq16, cs);
+            k_load<DK, DV>(fb, rec_rsrc(c + 1), kq_rsrc(c + 1), lane16, vq16, cs);
             state_chunk<DK, DV>(wf, fa, rec_rsrc(c + 1), h, ring, c, lane);
             __syncthreads();
-            k_load<DK, DV>(fa, rec_rsrc(c + 2), lane16, vq16, cs);
+            k_load<DK, DV>(fa, rec_rsrc(c + 2), kq_rsrc(c + 2), lane16, vq16, cs);
             state_chunk<DK, DV>(wf, fb, rec_rsrc(c + 2), h, ring, c + 1, lane);
             __syncthreads();
         }
@@ -828,9 +842,9 @@ __global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
 #pragma unroll
             for (int j = 0; j < 4; ++j) st[(16 * a + fq + j) * DV + col] = h[a][j];
     } else if (w == 1) {
-        out_wave<DK, DV, OUT, 0, 3>(p, ring, recs, NCr, len, lb, hv, cs, lane);
+        out_wave<DK, DV, OUT, 0, 3>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
     } else {
-        out_wave<DK, DV, OUT, 1, 2>(p, ring, recs, NCr, len, lb, hv, cs, lane);
+        out_wave<DK, DV, OUT, 1, 2>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
     }
 }
 
