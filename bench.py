@@ -589,6 +589,65 @@ def gated_rmsnorm(torch, gb, W, args):
     return dict(ms_per_call=ms, bytes_per_call=byts, gbs=byts / (ms / 1e3) / 1e9)
 
 
+def verify_gated_norm(torch, gb, W, args):
+    """Verify with the gated RMSNorm fused into its outputs
+    (gdn_verify_gated_norm) against the same two steps as separate launches
+    (gdn_verify, then gdn_gated_rmsnorm in place), over the cohort's 30 layer
+    pools; 20 back-to-back launches of each between HIP events."""
+    sh = W.COHORT
+    big, t, rng, act_rows = cohort_pools(torch, W, sh, L_POOL, 1001)
+    d = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
+                     out="f32")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5011)
+    z = torch.randn(t["o"].shape, generator=gen, device="cuda").to(torch.bfloat16)
+    w = (1.0 + 0.1 * torch.randn((L_POOL, sh.DV), generator=gen, device="cuda")).to(torch.bfloat16)
+    ins = [t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"], t["state"], t["cur"]]
+
+    def fused():
+        gb.gdn_verify_gated_norm(d, *ins, z, w, t["o"], active=t["active"], err=t["err"])
+
+    def split():
+        gb.gdn_verify(d, *ins, t["o"], t["active"], t["err"])
+        gb.gdn_gated_rmsnorm(d, t["o"], z, w, t["o"], active=t["active"])
+
+    # the fused commit + verify cycle, each call committing a fixed keep
+    keep = torch.from_numpy(W.keep_uniform(rng, sh, act_rows).astype(np.int32)).cuda()
+    prev = [t["x"], t["g"], t["beta"], keep, t["x"], t["conv_w"], None, t["conv_state"], t["g"],
+            t["beta"], t["state"], t["cur"]]
+
+    def lazy_fused():
+        gb.gdn_verify_lazy_gated_norm(d, *prev, z, w, t["o"], active=t["active"], err=t["err"])
+
+    def lazy_split():
+        gb.gdn_verify_lazy(d, *prev, t["o"], t["active"], t["err"])
+        gb.gdn_gated_rmsnorm(d, t["o"], z, w, t["o"], active=t["active"])
+
+    tm = Timer(torch)
+    res = {}
+    for name, fn in (("fused", fused), ("split", split), ("fused_again", fused),
+                     ("lazy_fused", lazy_fused), ("lazy_split", lazy_split)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        reps = 20
+        a = tm.ev()
+        for _ in range(reps):
+            fn()
+        b = tm.ev()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) / reps
+    assert int(t["err"].item()) == 0, "device error word set"
+    n_act = int(act_rows.sum())
+    byts = verify_bytes(sh, n_act, L_POOL) + L_POOL * (n_act * sh.T * sh.HV * sh.DV * 2 + sh.DV * 2)
+    ms = min(res["fused"], res["fused_again"])
+    del t, z, w
+    torch.cuda.empty_cache()
+    return dict(fused_ms=ms, split_ms=res["split"], bytes_per_call=byts,
+                gbs=byts / (ms / 1e3) / 1e9, lazy_fused_ms=res["lazy_fused"],
+                lazy_split_ms=res["lazy_split"])
+
+
 def cpu_baseline(W, budget_s=12.0):
     """The oracle as it stands (single-threaded C, float64) on a bounded
     sample of the headline workload: whole verify + commit layer-cycles of
@@ -637,7 +696,8 @@ def main():
     log("bench: %s on %s" % (gb.gdn_version(), torch.cuda.get_device_name(0)))
     sections = {"per_layer_graph": per_layer_graph, "solo": solo, "rewind": rewind,
                 "conv_step": conv_step, "prefill": prefill, "lazy": lazy_cycle,
-                "prefill_ragged": prefill_ragged, "gated_rmsnorm": gated_rmsnorm}
+                "prefill_ragged": prefill_ragged, "gated_rmsnorm": gated_rmsnorm,
+                "verify_gated_norm": verify_gated_norm}
     if args.only:
         print(json.dumps({args.only: sections[args.only](torch, gb, W, args)}), flush=True)
         return
@@ -651,7 +711,8 @@ def main():
                          ("rewind_b8_t4", rewind), ("conv_step_t1024", conv_step),
                          ("prefill_b1_4096_in_1024_calls", prefill),
                          ("prefill_ragged_b8_up_to_1024", prefill_ragged),
-                         ("gated_rmsnorm_b8_t2_l30", gated_rmsnorm)):
+                         ("gated_rmsnorm_b8_t2_l30", gated_rmsnorm),
+                         ("verify_gated_norm_b8_t2_l30", verify_gated_norm)):
             log("bench: %s" % name)
             extra[name] = fn(torch, gb, W, args)
             log("bench: %s -> %s" % (name, json.dumps(extra[name])))

@@ -78,6 +78,10 @@ _lib.gdn_rewind.argtypes = [_D] + [_vp] * 12
 _lib.gdn_verify_lazy.argtypes = [_D] + [_vp] * 16
 _lib.gdn_accept_greedy.argtypes = [_D] + [_vp] * 6
 _lib.gdn_gated_rmsnorm.argtypes = [_D, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp]
+# (dims, 8 inputs, z, norm_w, eps, y, active, err, stream); the lazy form adds
+# x_prev, g_prev, beta_prev and keep_prev in front of x
+_lib.gdn_verify_gated_norm.argtypes = [_D] + [_vp] * 10 + [ctypes.c_float] + [_vp] * 4
+_lib.gdn_verify_lazy_gated_norm.argtypes = [_D] + [_vp] * 14 + [ctypes.c_float] + [_vp] * 4
 _lib.gdn_prefill_ragged.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                     ctypes.c_size_t, _vp, _vp]
 _lib.gdn_prefill_chunked.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
@@ -91,11 +95,13 @@ _lib.gdn_version.restype = ctypes.c_char_p
 _lib.gdn_last_hip_error.argtypes = []
 _lib.gdn_last_hip_error.restype = ctypes.c_char_p
 for _n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
-           "gdn_accept_greedy", "gdn_gated_rmsnorm", "gdn_prefill_chunked", "gdn_prefill_ragged"):
+           "gdn_accept_greedy", "gdn_gated_rmsnorm", "gdn_verify_gated_norm",
+           "gdn_verify_lazy_gated_norm", "gdn_prefill_chunked", "gdn_prefill_ragged"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
-            "gdn_accept_greedy", "gdn_gated_rmsnorm", "gdn_prefill_chunked", "gdn_prefill_ragged",
+            "gdn_accept_greedy", "gdn_gated_rmsnorm", "gdn_verify_gated_norm",
+            "gdn_verify_lazy_gated_norm", "gdn_prefill_chunked", "gdn_prefill_ragged",
             "gdn_workspace_size", "gdn_status_string", "gdn_version", "gdn_last_hip_error")
 
 
@@ -224,6 +230,46 @@ def gdn_verify_lazy(d, x_prev, g_prev, beta_prev, keep_prev, x, conv_w, conv_b, 
         _arg(cur, "cur", s["cur"], torch.int32, True), _arg(o, "o", s["o"], O),
         _arg(active, "active", s["rows"], torch.uint8, True),
         _arg(err, "err", s["err"], torch.int32, True), _stream(stream)), "gdn_verify_lazy")
+
+
+def gdn_verify_gated_norm(d, x, conv_w, conv_b, conv_state, g, beta, state, cur, z, norm_w, y,
+                          eps=1e-6, active=None, err=None, stream=None):
+    """gdn_verify with the gated RMSNorm applied to the outputs in the same
+    launch: y = RMSNorm(o) * norm_w * SiLU(z) (z: o's shape in the act dtype,
+    norm_w: [L, DV] in the act dtype, y: o's shape in the out dtype)."""
+    torch, s = _torch(), _shapes(d)
+    A, O = _act_dtype(d.act), _act_dtype(d.out)
+    _check(_lib.gdn_verify_gated_norm(
+        ctypes.byref(d), _arg(x, "x", s["x"], A), _arg(conv_w, "conv_w", s["conv_w"], A),
+        _arg(conv_b, "conv_b", s["conv_b"], A, True),
+        _arg(conv_state, "conv_state", s["conv_state"], A), _arg(g, "g", s["g"], A),
+        _arg(beta, "beta", s["g"], A), _arg(state, "state", s["state"], torch.float32),
+        _arg(cur, "cur", s["cur"], torch.int32, True), _arg(z, "z", s["o"], A),
+        _arg(norm_w, "norm_w", (d.L, d.DV), A), float(eps), _arg(y, "y", s["o"], O),
+        _arg(active, "active", s["rows"], torch.uint8, True),
+        _arg(err, "err", s["err"], torch.int32, True), _stream(stream)), "gdn_verify_gated_norm")
+
+
+def gdn_verify_lazy_gated_norm(d, x_prev, g_prev, beta_prev, keep_prev, x, conv_w, conv_b,
+                               conv_state, g, beta, state, cur, z, norm_w, y, eps=1e-6,
+                               active=None, err=None, stream=None):
+    """gdn_verify_lazy with the gated RMSNorm of gdn_verify_gated_norm fused
+    into the new window's outputs."""
+    torch, s = _torch(), _shapes(d)
+    A, O = _act_dtype(d.act), _act_dtype(d.out)
+    _check(_lib.gdn_verify_lazy_gated_norm(
+        ctypes.byref(d), _arg(x_prev, "x_prev", s["x"], A, True),
+        _arg(g_prev, "g_prev", s["g"], A, True), _arg(beta_prev, "beta_prev", s["g"], A, True),
+        _arg(keep_prev, "keep_prev", s["rows"], torch.int32, True),
+        _arg(x, "x", s["x"], A), _arg(conv_w, "conv_w", s["conv_w"], A),
+        _arg(conv_b, "conv_b", s["conv_b"], A, True),
+        _arg(conv_state, "conv_state", s["conv_state"], A), _arg(g, "g", s["g"], A),
+        _arg(beta, "beta", s["g"], A), _arg(state, "state", s["state"], torch.float32),
+        _arg(cur, "cur", s["cur"], torch.int32, True), _arg(z, "z", s["o"], A),
+        _arg(norm_w, "norm_w", (d.L, d.DV), A), float(eps), _arg(y, "y", s["o"], O),
+        _arg(active, "active", s["rows"], torch.uint8, True),
+        _arg(err, "err", s["err"], torch.int32, True), _stream(stream)),
+        "gdn_verify_lazy_gated_norm")
 
 
 def gdn_workspace_size(d, chunk=64) -> int:

@@ -83,6 +83,78 @@ RecParams rec_params(const gdn_dims* d)
     return p;
 }
 
+// Gated-norm epilogue operands: all null (raw o) or z and w both given.
+struct NormEpi {
+    const void* z = nullptr;
+    const void* w = nullptr;
+    float eps = 0.0f;
+};
+
+gdn_status check_epi(const NormEpi& e)
+{
+    if (!e.w && !e.z) return GDN_OK;
+    if (!(e.eps >= 0.0f)) return GDN_E_SHAPE;
+    return check_ptrs({e.z, e.w}, {}, {});
+}
+
+gdn_status verify_impl(const gdn_dims* d, const void* x, const void* conv_w, const void* conv_b,
+                       const void* conv_state, const void* g, const void* beta, float* state,
+                       const int32_t* cur, void* o, const NormEpi& epi, const uint8_t* active,
+                       int32_t* err, void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    if (d->T > 4 || d->S < d->T + 1) return GDN_E_SHAPE;
+    st = check_ptrs({x, conv_w, conv_state, g, beta, state, o}, {conv_b}, {cur, err});
+    if (st != GDN_OK) return st;
+    st = check_epi(epi);
+    if (st != GDN_OK) return st;
+    RecParams p = rec_params(d);
+    p.x = x; p.conv_w = conv_w; p.conv_b = conv_b; p.conv_state = conv_state;
+    p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.active = active;
+    p.keep = nullptr; p.err = err; p.mode = gdn::REC_VERIFY;
+    p.z = epi.z; p.norm_w = epi.w; p.norm_eps = epi.eps;
+    return from_hip(gdn::launch_recurrent(p, d->DK, d->DV, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status verify_lazy_impl(const gdn_dims* d, const void* x_prev, const void* g_prev,
+                            const void* beta_prev, const int32_t* keep_prev, const void* x,
+                            const void* conv_w, const void* conv_b, void* conv_state,
+                            const void* g, const void* beta, float* state, const int32_t* cur,
+                            void* o, const NormEpi& epi, const uint8_t* active, int32_t* err,
+                            void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    if (d->T > 4) return GDN_E_SHAPE;
+    st = check_ptrs({x, conv_w, conv_state, g, beta, state, o}, {conv_b, x_prev, g_prev, beta_prev},
+                    {cur, keep_prev, err});
+    if (st != GDN_OK) return st;
+    if (keep_prev && (!x_prev || !g_prev || !beta_prev)) return GDN_E_NULL;
+    st = check_epi(epi);
+    if (st != GDN_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    RecParams p = rec_params(d);
+    p.x = x; p.conv_w = conv_w; p.conv_b = conv_b; p.conv_state = conv_state;
+    p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.active = active;
+    p.keep = keep_prev; p.err = err; p.mode = gdn::REC_LAZY;
+    p.z = epi.z; p.norm_w = epi.w; p.norm_eps = epi.eps;
+    // without a previous window nothing is replayed; its inputs are never
+    // used but every load of the kernel is unconditional, so point them at x
+    p.x_prev = keep_prev ? x_prev : x;
+    p.g_prev = keep_prev ? g_prev : g;
+    p.beta_prev = keep_prev ? beta_prev : beta;
+    st = from_hip(gdn::launch_recurrent(p, d->DK, d->DV, s));
+    if (st != GDN_OK || !keep_prev) return st;
+    // The conv cache is shifted by a second launch, after every wave has read
+    // the old cache.
+    WinParams w{};
+    w.x = x_prev; w.conv_state = conv_state; w.cur = const_cast<int32_t*>(cur); w.keep = keep_prev;
+    w.active = nullptr; w.err = err; w.L = d->L; w.B = d->B; w.T = d->T; w.S = d->S;
+    w.C = p.C; w.act = d->act; w.mode = gdn::WIN_REWIND;
+    return from_hip(gdn::launch_window(w, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,16 +204,20 @@ gdn_status gdn_verify(const gdn_dims* d, const void* x, const void* conv_w, cons
                       const int32_t* cur, void* o, const uint8_t* active, int32_t* err,
                       void* stream)
 {
-    gdn_status st = check_dims(d);
-    if (st != GDN_OK) return st;
-    if (d->T > 4 || d->S < d->T + 1) return GDN_E_SHAPE;
-    st = check_ptrs({x, conv_w, conv_state, g, beta, state, o}, {conv_b}, {cur, err});
-    if (st != GDN_OK) return st;
-    RecParams p = rec_params(d);
-    p.x = x; p.conv_w = conv_w; p.conv_b = conv_b; p.conv_state = conv_state;
-    p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.active = active;
-    p.keep = nullptr; p.err = err; p.mode = gdn::REC_VERIFY;
-    return from_hip(gdn::launch_recurrent(p, d->DK, d->DV, static_cast<hipStream_t>(stream)));
+    return verify_impl(d, x, conv_w, conv_b, conv_state, g, beta, state, cur, o, NormEpi{}, active, err,
+                       stream);
+}
+
+gdn_status gdn_verify_gated_norm(const gdn_dims* d, const void* x, const void* conv_w,
+                                 const void* conv_b, const void* conv_state, const void* g,
+                                 const void* beta, float* state, const int32_t* cur,
+                                 const void* z, const void* norm_w, float norm_eps, void* y,
+                                 const uint8_t* active, int32_t* err, void* stream)
+{
+    if (!z || !norm_w) return GDN_E_NULL;
+    NormEpi e;
+    e.z = z; e.w = norm_w; e.eps = norm_eps;
+    return verify_impl(d, x, conv_w, conv_b, conv_state, g, beta, state, cur, y, e, active, err, stream);
 }
 
 gdn_status gdn_commit(const gdn_dims* d, const void* x, void* conv_state, int32_t* cur,
@@ -199,32 +275,23 @@ gdn_status gdn_verify_lazy(const gdn_dims* d, const void* x_prev, const void* g_
                            const void* g, const void* beta, float* state, const int32_t* cur,
                            void* o, const uint8_t* active, int32_t* err, void* stream)
 {
-    gdn_status st = check_dims(d);
-    if (st != GDN_OK) return st;
-    if (d->T > 4) return GDN_E_SHAPE;
-    st = check_ptrs({x, conv_w, conv_state, g, beta, state, o}, {conv_b, x_prev, g_prev, beta_prev},
-                    {cur, keep_prev, err});
-    if (st != GDN_OK) return st;
-    if (keep_prev && (!x_prev || !g_prev || !beta_prev)) return GDN_E_NULL;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    RecParams p = rec_params(d);
-    p.x = x; p.conv_w = conv_w; p.conv_b = conv_b; p.conv_state = conv_state;
-    p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.active = active;
-    p.keep = keep_prev; p.err = err; p.mode = gdn::REC_LAZY;
-    // without a previous window nothing is replayed; its inputs are never
-    // used but every load of the kernel is unconditional, so point them at x
-    p.x_prev = keep_prev ? x_prev : x;
-    p.g_prev = keep_prev ? g_prev : g;
-    p.beta_prev = keep_prev ? beta_prev : beta;
-    st = from_hip(gdn::launch_recurrent(p, d->DK, d->DV, s));
-    if (st != GDN_OK || !keep_prev) return st;
-    // The conv cache is shifted by a second launch, after every wave has read
-    // the old cache.
-    WinParams w{};
-    w.x = x_prev; w.conv_state = conv_state; w.cur = const_cast<int32_t*>(cur); w.keep = keep_prev;
-    w.active = nullptr; w.err = err; w.L = d->L; w.B = d->B; w.T = d->T; w.S = d->S;
-    w.C = p.C; w.act = d->act; w.mode = gdn::WIN_REWIND;
-    return from_hip(gdn::launch_window(w, s));
+    return verify_lazy_impl(d, x_prev, g_prev, beta_prev, keep_prev, x, conv_w, conv_b, conv_state, g, beta,
+                            state, cur, o, NormEpi{}, active, err, stream);
+}
+
+gdn_status gdn_verify_lazy_gated_norm(const gdn_dims* d, const void* x_prev, const void* g_prev,
+                                      const void* beta_prev, const int32_t* keep_prev, const void* x,
+                                      const void* conv_w, const void* conv_b, void* conv_state,
+                                      const void* g, const void* beta, float* state,
+                                      const int32_t* cur, const void* z, const void* norm_w,
+                                      float norm_eps, void* y, const uint8_t* active, int32_t* err,
+                                      void* stream)
+{
+    if (!z || !norm_w) return GDN_E_NULL;
+    NormEpi e;
+    e.z = z; e.w = norm_w; e.eps = norm_eps;
+    return verify_lazy_impl(d, x_prev, g_prev, beta_prev, keep_prev, x, conv_w, conv_b, conv_state, g, beta,
+                            state, cur, y, e, active, err, stream);
 }
 
 gdn_status gdn_accept_greedy(const gdn_dims* d, const int32_t* draft_ids, const int32_t* target_ids,

@@ -39,7 +39,10 @@ struct RecParams {
     uint32_t flags;
     int32_t mode;
     int32_t groups;     // L * B * HK
-    int32_t per_group;  // (HV / HK) * column slices per head
+    int32_t per_group;  // workgroups per (layer, row, qk head)
+    const void* z;      // gated RMSNorm epilogue: gate input [L][B][T][HV][DV] (act)
+    const void* norm_w; // and weight [L][DV] (act); null: o is written raw
+    float norm_eps;
 };
 
 // ---------------------------------------------------------------------------

@@ -62,19 +62,39 @@ __device__ __forceinline__ float pick4(const float (&v)[4], int i)
 // Z = [conv cache ; previous x[0..keep) ; new x[0..T)], so the committed conv
 // cache (rows keep..keep+2 of the previous window) is simply rows keep..keep+2
 // of Z and one conv pass covers both windows.
-template <int DK, int DV, int ACT, bool LAZY>
-__global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
+//
+// NORM: the gated RMSNorm that follows the mixer ("MTP inference: review and
+// commit structure" (eole docs), Functional commits item 4) is applied to
+// every output before it is stored, y[j] = o[j] / sqrt(mean_j(o^2) + eps) *
+// w[l][j] * SiLU(z[j]), so the raw o never goes to memory.  The mean runs over
+// all d_v columns of a head, so one workgroup holds the NS column-slice waves
+// of a head (wave w = slice w) and adds their partial sums of squares through
+// LDS, one barrier per output token.
+template <int DV>
+constexpr int waves_per_head()
+{
+    return DV / (DV < 32 ? DV : 32);
+}
+
+template <int DK, int DV, int ACT, bool LAZY, bool NORM>
+__global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurrent_kernel(RecParams p)
 {
     constexpr int SW = DV < 32 ? DV : 32;  // columns per wave
     constexpr int NS = DV / SW;            // column slices per head
     constexpr int JL = SW / 4;             // lanes across one row segment
     constexpr int IG = 64 / JL;            // row groups per wave
     constexpr int RPL = DK / IG;           // rows held per lane
-    constexpr int NCH = 2 * DK + SW;       // conv channels this wave needs
     constexpr int MAXT = LAZY ? 8 : 4;     // tokens one wave runs
+    constexpr int NW = NORM ? NS : 1;      // waves per workgroup
+    // conv channels of the workgroup: q and k of the qk head, then the v
+    // channels of its one slice, or (NORM) of all NS slices, whose waves share
+    // the q and k conv
+    constexpr int NCH = 2 * DK + (NORM ? DV : SW);
     static_assert(RPL >= 1 && DK % IG == 0, "tile shape");
 
     __shared__ float ys[MAXT][NCH];
+    __shared__ float ssq[NORM ? MAXT : 1][NW];   // per-slice sums of o^2 (NORM)
+    __shared__ float gzw[NW][NORM ? 4 : 1][NORM ? SW : 1];   // w[j] * SiLU(z[t][j]) (NORM)
 
     // ---- block -> (layer, row, qk head, value head, slice), XCD-aware ----
     const int bid = blockIdx.x;
@@ -87,10 +107,11 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
     const int lb = grp / p.HK;  // l * B + b
     const int b = lb % p.B;
     const int gsz = p.HV / p.HK;
-    const int slice = r_in % NS;
-    const int hv = m * gsz + r_in / NS;
+    const int wid = NORM ? static_cast<int>(threadIdx.x >> 6) : 0;
+    const int slice = NORM ? wid : r_in % NS;
+    const int hv = NORM ? m * gsz + r_in : m * gsz + r_in / NS;
 
-    const int lane = threadIdx.x;
+    const int lane = NORM ? static_cast<int>(threadIdx.x & 63) : static_cast<int>(threadIdx.x);
     const int j4 = lane % JL;
     const int ig = lane / JL;
     const int col0 = slice * SW + j4 * 4;
@@ -139,17 +160,19 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
     const size_t srow = static_cast<size_t>(lb) * 3;          // conv_state row 0
     const bool has_bias = p.conv_b != nullptr;
     const void* bptr = has_bias ? p.conv_b : p.conv_w;
-    constexpr int NG = (NCH + 63) / 64;
+    constexpr int NG = (NCH + 64 * NW - 1) / (64 * NW);   // channel groups per wave
+    // channel of group n in this lane: lane + 64 * (wid + NW * n)
+    const int vcol = NORM ? 0 : slice * SW;   // first v column of the channel set
     constexpr int NROW = MAXT + 3;   // window rows per channel
     float wv[NG][4];
     float win[NG][NROW];
     float bias[NG];
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
-        const int ch = min(lane + 64 * n, NCH - 1);
+        const int ch = min(lane + 64 * (wid + NW * n), NCH - 1);
         const int c = ch < DK ? m * DK + ch
                     : (ch < 2 * DK ? p.HK * DK + m * DK + (ch - DK)
-                                   : 2 * p.HK * DK + hv * DV + slice * SW + (ch - 2 * DK));
+                                   : 2 * p.HK * DK + hv * DV + vcol + (ch - 2 * DK));
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             wv[n][j] = load_act<ACT>(p.conv_w, (static_cast<size_t>(l) * C + c) * 4 + j);
@@ -200,6 +223,20 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
         }
     }
 
+    // ---- gated-norm operands of this lane's 4 columns (NORM); they are folded
+    // into w * SiLU(z) in LDS with the conv, so no register holds them
+    // through the recurrence ----
+    float zv[4][4], nw[4];
+    if constexpr (NORM) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                zv[t][c] = load_act<ACT>(p.z, ((xrow + min(t, p.T - 1)) * p.HV + hv) * DV + col0 + c);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) nw[c] = load_act<ACT>(p.norm_w, static_cast<size_t>(l) * DV + col0 + c);
+    }
+
     // ---- the state slice: every load issued before any use ----
     const size_t tile = static_cast<size_t>(DK) * DV;
     float* st_lb = p.state + static_cast<size_t>(lb) * p.S * p.HV * tile;
@@ -213,7 +250,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
     const bool use_silu = (p.flags & FLAG_SILU) != 0;
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
-        const int ch = lane + 64 * n;
+        const int ch = lane + 64 * (wid + NW * n);
 #pragma unroll
         for (int t = 0; t < MAXT; ++t) {
             float acc = wv[n][0] * win[n][t];
@@ -224,6 +261,13 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
             const float sv = silu(acc);
             if (ch < NCH && t < nsteps) ys[t][ch] = use_silu ? sv : acc;
         }
+    }
+    if constexpr (NORM) {
+        if (ig == 0)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) gzw[wid][t][j4 * 4 + c] = nw[c] * silu(zv[t][c]);
     }
     __syncthreads();
 
@@ -279,7 +323,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
         float u[4], oo[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const float vj = ys[t][2 * DK + j4 * 4 + c];
+            const float vj = ys[t][2 * DK + (NORM ? slice * SW : 0) + j4 * 4 + c];
             u[c] = bt * (vj - a * (pp[c] * inv_nk));
             oo[c] = p.scale * (a * (rr[c] * inv_nq) + u[c] * kqn);
         }
@@ -291,6 +335,26 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
         }
 
         const int tout = LAZY ? t - kp : t;   // token of the window o belongs to
+        if constexpr (NORM) {
+            if (tout >= 0) {   // uniform over the workgroup: kp is the row's
+                // every lane holds its row group's copy of the 4 columns; the
+                // JL lanes of a row group cover the wave's SW columns
+                float ss = oo[0] * oo[0];
+#pragma unroll
+                for (int c = 1; c < 4; ++c) ss = fmaf(oo[c], oo[c], ss);
+#pragma unroll
+                for (int off = 1; off < JL; off <<= 1) ss += __shfl_xor(ss, off, 64);
+                if (lane == 0) ssq[t][wid] = ss;
+                __syncthreads();
+                float tot = ssq[t][0];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) tot += ssq[t][w];
+                const float rn = 1.0f / sqrtf(tot / static_cast<float>(DV) + p.norm_eps);
+                const int tz = tout < 4 ? tout : 3;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) oo[c] = oo[c] * rn * gzw[wid][tz][j4 * 4 + c];
+            }
+        }
         if (LAZY && t + 1 == kp) {
             // committed state of the previous window, in place
             float* dst = st_lb + (static_cast<size_t>(slot0) * p.HV + hv) * tile + col0;
@@ -335,6 +399,12 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecParams p)
 // up to T steps between its single read and single write of the slice and
 // needs the other waves to cover that, so it runs uncapped.
 constexpr int kVerifyWgPerCU = 4;   // one wave per SIMD
+// Verify with the fused norm runs the NS waves of a head as one workgroup
+// with a barrier per token, so a wave stalls for its siblings; two such
+// workgroups per CU (two waves per SIMD) cover that (B8/T2 cohort, 30
+// layers: one per CU 253 us, two 204 us, three 203 us, uncapped 204 us,
+// against 216-224 us for verify plus the separate norm launch).
+constexpr int kVerifyNormWgPerCU = 2;
 constexpr int kRewindWgPerCU = 0;   // no cap
 constexpr int kLazyWgPerCU = 0;     // no cap (replay steps between read and write)
 
@@ -356,31 +426,62 @@ static size_t occupancy_lds_bytes(size_t static_bytes, int wg_per_cu)
     return total > static_bytes ? total - static_bytes : 0;
 }
 
+// Static LDS of a kernel, queried once per process per instantiation.
+template <typename K>
+static size_t static_lds_of(K kernel)
+{
+    static std::atomic<long long> cached{-1};
+    long long v = cached.load(std::memory_order_relaxed);
+    if (v < 0) {
+        hipFuncAttributes a{};
+        if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(kernel)) != hipSuccess) {
+            clear_stale_error();
+            return 0;   // no cap can be derived; the launch then runs uncapped
+        }
+        v = static_cast<long long>(a.sharedSizeBytes);
+        cached.store(v, std::memory_order_relaxed);
+    }
+    return static_cast<size_t>(v);
+}
+
+template <int DK, int DV, int ACT, bool LAZY, bool NORM>
+static void launch_one(const RecParams& p, dim3 grid, int threads, int cap, hipStream_t s)
+{
+    auto k = recurrent_kernel<DK, DV, ACT, LAZY, NORM>;
+    const size_t st = cap > 0 ? static_lds_of(k) : 0;
+    const size_t dyn = cap > 0 && st > 0 ? occupancy_lds_bytes(st, cap) : 0;
+    hipLaunchKernelGGL(k, grid, dim3(threads), dyn, s, p);
+}
+
+template <int DK, int DV, bool LAZY, bool NORM>
+static void launch_rec_act(const RecParams& p, dim3 grid, int threads, int cap, hipStream_t s)
+{
+    if (p.act == ACT_BF16) launch_one<DK, DV, ACT_BF16, LAZY, NORM>(p, grid, threads, cap, s);
+    else launch_one<DK, DV, ACT_F32, LAZY, NORM>(p, grid, threads, cap, s);
+}
+
 template <int DK, int DV>
 static hipError_t launch_rec(RecParams p, hipStream_t s)
 {
     constexpr int SW = DV < 32 ? DV : 32;
     constexpr int NS = DV / SW;
     const bool lazy = p.mode == REC_LAZY;
-    const size_t static_lds = sizeof(float) * (lazy ? 8 : 4) * (2 * DK + SW);   // ys[MAXT][NCH]
+    const bool norm = p.norm_w != nullptr;
+    const int nw = norm ? NS : 1;   // waves per workgroup
     p.groups = p.L * p.B * p.HK;
-    p.per_group = (p.HV / p.HK) * NS;
+    p.per_group = (p.HV / p.HK) * (norm ? 1 : NS);
     const long long blocks = static_cast<long long>((p.groups + 7) / 8) * 8 * p.per_group;
     if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const int cap = p.mode == REC_VERIFY ? kVerifyWgPerCU : p.mode == REC_LAZY ? kLazyWgPerCU : kRewindWgPerCU;
-    const size_t dyn = occupancy_lds_bytes(static_lds, cap);
+    int cap = p.mode == REC_VERIFY ? kVerifyWgPerCU : p.mode == REC_LAZY ? kLazyWgPerCU : kRewindWgPerCU;
+    if (norm && nw > 1 && p.mode == REC_VERIFY) cap = kVerifyNormWgPerCU;
     const dim3 grid(static_cast<unsigned>(blocks));
     clear_stale_error();
     if (lazy) {
-        if (p.act == ACT_BF16)
-            hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_BF16, true>), grid, dim3(64), dyn, s, p);
-        else
-            hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_F32, true>), grid, dim3(64), dyn, s, p);
+        if (norm) launch_rec_act<DK, DV, true, true>(p, grid, 64 * nw, cap, s);
+        else launch_rec_act<DK, DV, true, false>(p, grid, 64, cap, s);
     } else {
-        if (p.act == ACT_BF16)
-            hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_BF16, false>), grid, dim3(64), dyn, s, p);
-        else
-            hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT_F32, false>), grid, dim3(64), dyn, s, p);
+        if (norm) launch_rec_act<DK, DV, false, true>(p, grid, 64 * nw, cap, s);
+        else launch_rec_act<DK, DV, false, false>(p, grid, 64, cap, s);
     }
     return hipGetLastError();
 }

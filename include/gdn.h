@@ -200,6 +200,32 @@ gdn_status gdn_accept_greedy(const gdn_dims* d, const int32_t* draft_ids, const 
 gdn_status gdn_gated_rmsnorm(const gdn_dims* d, const void* o, const void* z, const void* w,
                              float eps, void* y, const uint8_t* active, void* stream);
 
+/* gdn_verify with the gated RMSNorm of gdn_gated_rmsnorm applied to every
+ * output inside the same launch ([P2] Functional commits item 4), so the raw
+ * mixer output never goes to memory: y[t] (out dtype, [L][B][T][HV][DV])
+ * receives RMSNorm(o[t]) * w * SiLU(z[t]) for every active row; z (act dtype,
+ * same shape as y) and norm_w (act dtype, [L][DV]) must be given, norm_eps
+ * >= 0.  The mean square is taken over the fp32 outputs before any rounding.
+ * Candidate states, slots and error bits are exactly those of gdn_verify
+ * (bit for bit).  err: GDN_ERR_SLOT. */
+gdn_status gdn_verify_gated_norm(const gdn_dims* d, const void* x, const void* conv_w,
+                                 const void* conv_b, const void* conv_state, const void* g,
+                                 const void* beta, float* state, const int32_t* cur,
+                                 const void* z, const void* norm_w, float norm_eps, void* y,
+                                 const uint8_t* active, int32_t* err, void* stream);
+
+/* gdn_verify_lazy with the same fused gated RMSNorm on the new window's
+ * outputs (y, z, norm_w, norm_eps as for gdn_verify_gated_norm).  The
+ * committed state, conv cache and error bits are exactly those of
+ * gdn_verify_lazy.  err: GDN_ERR_KEEP, GDN_ERR_SLOT. */
+gdn_status gdn_verify_lazy_gated_norm(const gdn_dims* d, const void* x_prev, const void* g_prev,
+                                      const void* beta_prev, const int32_t* keep_prev, const void* x,
+                                      const void* conv_w, const void* conv_b, void* conv_state,
+                                      const void* g, const void* beta, float* state,
+                                      const int32_t* cur, const void* z, const void* norm_w,
+                                      float norm_eps, void* y, const uint8_t* active, int32_t* err,
+                                      void* stream);
+
 /* Chunked prompt prefill of the same recurrence ([P1] Measurements:
  * 1,024-token layer-major prefill calls; [P2] Verification and limits: the
  * chunk recurrence equals the sequential one up to rounding).  y holds the

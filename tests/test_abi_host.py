@@ -180,6 +180,41 @@ def test_gated_rmsnorm_validation(lib):
     assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 1e-6, FAKE, None, None) == 2
 
 
+def test_verify_gated_norm_validation(lib):
+    """Host checks of verify / fused commit + verify with the gated-norm
+    epilogue: the norm operands are required, aligned, eps >= 0, and the
+    window checks of the plain calls still apply.  No call reaches a launch."""
+    fv = lib.gdn_verify_gated_norm
+    fv.argtypes = ([ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 10 + [ctypes.c_float] +
+                   [ctypes.c_void_p] * 4)
+    fl = lib.gdn_verify_lazy_gated_norm
+    fl.argtypes = ([ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 14 + [ctypes.c_float] +
+                   [ctypes.c_void_p] * 4)
+
+    def v(d, z=FAKE, w=FAKE, eps=1e-6, y=FAKE, cur=None):
+        return fv(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, cur, z, w, eps, y,
+                  None, None, None)
+
+    def lz(d, z=FAKE, w=FAKE, eps=1e-6, y=FAKE):
+        return fl(ctypes.byref(d), None, None, None, None, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                  FAKE, None, z, w, eps, y, None, None, None)
+
+    d = good()
+    for call in (v, lz):
+        assert call(d, z=None) == 1             # gate input required
+        assert call(d, w=None) == 1             # norm weight required
+        assert call(d, y=None) == 1             # outputs required
+        assert call(d, w=FAKE + 8) == 4         # 16-byte alignment
+        assert call(d, eps=-1.0) == 2           # eps >= 0
+        assert call(d, eps=float("nan")) == 2
+    assert v(d, cur=FAKE + 2) == 4
+    d.T = 5
+    assert v(d) == 2 and lz(d) == 2             # windows are at most 4 tokens
+    d = good()
+    d.S = 2                                     # verify needs S >= T + 1
+    assert v(d) == 2
+
+
 def test_status_strings_and_version(lib):
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_version.restype = ctypes.c_char_p
