@@ -426,15 +426,18 @@ static size_t occupancy_lds_bytes(size_t static_bytes, int wg_per_cu)
     return total > static_bytes ? total - static_bytes : 0;
 }
 
-// Static LDS of a kernel, queried once per process per instantiation.
-template <typename K>
-static size_t static_lds_of(K kernel)
+// Static LDS of one kernel instantiation, queried once per process (the
+// cache is a static of this function template, so each instantiation has its
+// own).
+template <int DK, int DV, int ACT, bool LAZY, bool NORM>
+static size_t static_lds()
 {
     static std::atomic<long long> cached{-1};
     long long v = cached.load(std::memory_order_relaxed);
     if (v < 0) {
         hipFuncAttributes a{};
-        if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(kernel)) != hipSuccess) {
+        if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(recurrent_kernel<DK, DV, ACT, LAZY, NORM>)) !=
+            hipSuccess) {
             clear_stale_error();
             return 0;   // no cap can be derived; the launch then runs uncapped
         }
@@ -447,10 +450,9 @@ static size_t static_lds_of(K kernel)
 template <int DK, int DV, int ACT, bool LAZY, bool NORM>
 static void launch_one(const RecParams& p, dim3 grid, int threads, int cap, hipStream_t s)
 {
-    auto k = recurrent_kernel<DK, DV, ACT, LAZY, NORM>;
-    const size_t st = cap > 0 ? static_lds_of(k) : 0;
+    const size_t st = cap > 0 ? static_lds<DK, DV, ACT, LAZY, NORM>() : 0;
     const size_t dyn = cap > 0 && st > 0 ? occupancy_lds_bytes(st, cap) : 0;
-    hipLaunchKernelGGL(k, grid, dim3(threads), dyn, s, p);
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT, LAZY, NORM>), grid, dim3(threads), dyn, s, p);
 }
 
 template <int DK, int DV, bool LAZY, bool NORM>
