@@ -37,6 +37,7 @@ gdn_status check_dims(const gdn_dims* d)
     // inside their limits.
     const long long C = channels(d);
     if (static_cast<long long>(d->L) * d->B > 65535) return GDN_E_SHAPE;
+    if (static_cast<long long>(d->L) * d->B * d->HV > (1LL << 30)) return GDN_E_SHAPE;   // 32-bit tile counts
     if (static_cast<long long>(d->HV) * d->DK * d->DV * d->S * d->B * d->L > (1LL << 40))
         return GDN_E_SHAPE;
     if (C * d->T > (1LL << 31)) return GDN_E_SHAPE;

@@ -180,6 +180,16 @@ def test_gated_rmsnorm_validation(lib):
     assert f(ctypes.byref(d), FAKE, FAKE, FAKE, 1e-6, FAKE, None, None) == 2
 
 
+def test_tile_counts_fit_32_bits(lib):
+    """(layer, row, head) tile counts beyond 2^30 are refused on the host, so
+    no grid size or tile index can overflow a 32-bit counter."""
+    f = lib.gdn_verify
+    f.argtypes = [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 12
+    d = Dims(1, 32768, 2, 65536, 65536, 16, 16, 4, 1, 1, 0, 1.0, 1e-6, 3)   # state size in range
+    assert f(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
+             None) == 2
+
+
 def test_verify_gated_norm_validation(lib):
     """Host checks of verify / fused commit + verify with the gated-norm
     epilogue: the norm operands are required, aligned, eps >= 0, and the

@@ -113,6 +113,24 @@ def test_prefill_carried_state_and_split_calls_bit_exact():
     assert out_err(o1, o_r) <= 2e-3 and state_err(st1, st_r) <= 2e-3
 
 
+def test_prefill_4096_tokens_in_one_call():
+    """The whole 4,096-token prompt in one call (64 chunks: the longest record
+    chain a call builds here) from a random N(0, 0.1^2) state, 4 value heads
+    on 2 qk heads at d = 128, against the token-sequential oracle; equal bit
+    for bit to the same prompt in four 1,024-token calls."""
+    sh = W.PREFILL.with_(HV=4, HK=2)
+    inp = W.prefill_inputs(sh, seed=3150, tokens=W.PREFILL_TOKENS)
+    inp["state"] = W.random_state(sh, seed=3151)
+    st1, o1 = gpu_prefill(sh, inp, T=W.PREFILL_TOKENS, calls=[W.PREFILL_TOKENS])
+    st4, o4 = gpu_prefill(sh, inp, T=W.PREFILL_TOKENS, calls=[1024] * 4)
+    assert np.array_equal(st1, st4) and np.array_equal(o1, o4)
+    st_r, o_r, err = oracle_prefill(sh, inp, T=W.PREFILL_TOKENS)
+    assert err == 0
+    e_o, e_s = out_err(o1, o_r), state_err(st1, st_r)
+    print("prefill 4096 in one call: out err %.3e state err %.3e" % (e_o, e_s))
+    assert e_o <= 2e-3 and e_s <= 2e-3
+
+
 def test_prefill_bf16_output_and_scale():
     sh = W.Shape("pfo", L=2, B=1, T=200, HV=2, HK=1, DK=128, DV=64, S=1, out="bf16")
     inp = W.prefill_inputs(sh, seed=3300)
