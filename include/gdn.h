@@ -1,8 +1,9 @@
 /*
  * gdn.h -- C ABI of libgdn.so: the Gated DeltaNet verify / commit / rewind /
  * conv-step / chunked-prefill path of speculative multi-token-prediction
- * (MTP) decoding, as hand-written HIP kernels for AMD Instinct MI355X
- * (gfx950).
+ * (MTP) decoding, with the commit folded into the next verify, device greedy
+ * acceptance and the gated RMSNorm epilogue, as hand-written HIP kernels for
+ * AMD Instinct MI355X (gfx950).
  *
  * Page sources (title, then section):
  *  [P1] "perf(qwen): full-context MTP draft prefill and replay-free rewind"
@@ -41,7 +42,8 @@
  *    on an inactive row) leave that (layer, row) untouched and OR a
  *    GDN_ERR_* bit into *err when err is not NULL.  The library never
  *    clears *err.
- *  - Outputs (o, y, workspace) must not alias any input.
+ *  - Outputs (o, y, workspace) must not alias any input, except where an
+ *    entry point allows it (gdn_gated_rmsnorm: y may be o).
  *  - The library holds no per-call global state: calls on distinct streams
  *    over disjoint buffers are independent.
  *
