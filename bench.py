@@ -680,9 +680,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this path has no cross-GPU exchange and the "
-              "build runs on single-GPU boxes; --gpus %d is not supported" % max(args.gpus, world),
-              file=sys.stderr)
+        print("bench.py measures a single GPU: the path has no cross-GPU exchange, so "
+              "--gpus %d is not supported" % max(args.gpus, world), file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -77,7 +77,7 @@ typedef enum {
     GDN_E_SHAPE = 2,       /* a size is out of the supported range */
     GDN_E_DTYPE = 3,       /* act/out is not GDN_F32 or GDN_BF16 */
     GDN_E_ALIGN = 4,       /* a pointer breaks the alignment rule above */
-    GDN_E_UNSUPPORTED = 5, /* a valid request this build does not implement */
+    GDN_E_UNSUPPORTED = 5, /* a valid request the library does not implement */
     GDN_E_WORKSPACE = 6,   /* workspace NULL or smaller than gdn_workspace_size */
     GDN_E_HIP = 7          /* the HIP runtime reported a launch failure */
 } gdn_status;
