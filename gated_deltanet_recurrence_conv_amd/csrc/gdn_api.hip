@@ -20,7 +20,13 @@ bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int channels(const gdn_dims* d) { return 2 * d->HK * d->DK + d->HV * d->DV; }
+long long channels64(const gdn_dims* d)
+{
+    return 2LL * d->HK * d->DK + static_cast<long long>(d->HV) * d->DV;
+}
+
+// Conv channels; fits int32 once check_dims has passed (C * T <= 2^31).
+int channels(const gdn_dims* d) { return static_cast<int>(channels64(d)); }
 
 // Checks shared by every call.
 gdn_status check_dims(const gdn_dims* d)
@@ -35,7 +41,7 @@ gdn_status check_dims(const gdn_dims* d)
     if (d->KCONV != 4) return GDN_E_SHAPE;
     // Keep every element index of every array inside int64 and the grids
     // inside their limits.
-    const long long C = channels(d);
+    const long long C = channels64(d);
     if (static_cast<long long>(d->L) * d->B > 65535) return GDN_E_SHAPE;
     if (static_cast<long long>(d->L) * d->B * d->HV > (1LL << 30)) return GDN_E_SHAPE;   // 32-bit tile counts
     if (static_cast<long long>(d->HV) * d->DK * d->DV * d->S * d->B * d->L > (1LL << 40))

@@ -190,6 +190,16 @@ def test_tile_counts_fit_32_bits(lib):
              None) == 2
 
 
+def test_huge_head_counts_refused_without_overflow(lib):
+    """Channel counts beyond 32 bits (2*HK*DK + HV*DV) are computed in 64 bits
+    and refused."""
+    f = lib.gdn_verify
+    f.argtypes = [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 12
+    d = Dims(1, 1, 2, 1 << 25, 1 << 25, 128, 128, 4, 3, 1, 0, 1.0, 1e-6, 3)
+    assert f(ctypes.byref(d), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
+             None) == 2
+
+
 def test_verify_gated_norm_validation(lib):
     """Host checks of verify / fused commit + verify with the gated-norm
     epilogue: the norm operands are required, aligned, eps >= 0, and the
