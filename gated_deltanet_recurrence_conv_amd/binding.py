@@ -128,6 +128,9 @@ def _arg(t, name, shape=None, dtype=None, optional=False):
         raise TypeError("%s: expected a torch.Tensor or a device address" % name)
     if t.device.type != "cuda":
         raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if t.device.index is not None and t.device.index != torch.cuda.current_device():
+        raise ValueError("%s is on %s but the current device is cuda:%d (launches go to the "
+                         "current device)" % (name, t.device, torch.cuda.current_device()))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
