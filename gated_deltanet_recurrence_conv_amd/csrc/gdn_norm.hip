@@ -5,68 +5,118 @@
 // For every (layer, row, token, value head):
 //     y[j] = o[j] / sqrt(mean_j(o^2) + eps) * w[l][j] * SiLU(z[j]).
 //
-// Streaming work (o and z read once, y written once): one 64-lane wave per
-// (layer, row, token, head), lanes over the d_v columns so every access is a
-// contiguous run, the mean square reduced across the wave.  y may alias o:
-// each lane reads its columns before the reduction and writes them after.
+// Streaming work (o and z read once, y written once): 8 consecutive columns
+// per lane moved as 16- or 32-byte vectors, DV / 8 lanes per (layer, row,
+// token, head) row and 64 / (DV / 8) rows per wave, the mean square reduced
+// across a row's lanes.  y may alias o: every lane reads its columns before
+// the reduction and writes them after it.
 #include "gdn_internal.h"
 
 namespace gdn {
 
-template <int ACT, int OUT>
-__global__ __launch_bounds__(256) void gated_rmsnorm_kernel(NormParams p)
-{
-    constexpr int MAXV = 2;   // columns per lane (d_v <= 128)
-    const long long wave = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const long long total = static_cast<long long>(p.L) * p.B * p.T * p.HV;
-    if (wave >= total) return;
-    const int b = static_cast<int>((wave / (static_cast<long long>(p.T) * p.HV)) % p.B);
-    const int l = static_cast<int>(wave / (static_cast<long long>(p.B) * p.T * p.HV));
-    if (p.active && p.active[b] == 0) return;
-    const int DV = p.DV;
-    const size_t base = static_cast<size_t>(wave) * DV;
+namespace {
 
-    float ov[MAXV], zv[MAXV], wv[MAXV];
-    float ss = 0.f;
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, size_t idx, float* v)
+{
+    if constexpr (DT == ACT_BF16) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-        const int j = lane + 64 * i;
-        const bool in = j < DV;
-        const int jj = in ? j : 0;
-        ov[i] = in ? load_act<OUT>(p.o, base + jj) : 0.f;
-        zv[i] = load_act<ACT>(p.z, base + jj);
-        wv[i] = load_act<ACT>(p.w, static_cast<size_t>(l) * DV + jj);
-        ss = fmaf(ov[i], ov[i], ss);
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) ss += __shfl_xor(ss, off, 64);
-    const float r = 1.0f / sqrtf(ss / static_cast<float>(DV) + p.eps);
-#pragma unroll
-    for (int i = 0; i < MAXV; ++i) {
-        const int j = lane + 64 * i;
-        if (j >= DV) continue;
-        const float yv = ov[i] * r * wv[i] * silu(zv[i]);
-        if constexpr (OUT == ACT_BF16) static_cast<uint16_t*>(p.y)[base + j] = f32_to_bf16_bits(yv);
-        else static_cast<float*>(p.y)[base + j] = yv;
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
 }
+
+template <int DT>
+__device__ __forceinline__ void store8(void* base, size_t idx, const float* v)
+{
+    if constexpr (DT == ACT_BF16) {
+        uint4 raw;
+        raw.x = f32x2_to_bf16x2(v[0], v[1]);
+        raw.y = f32x2_to_bf16x2(v[2], v[3]);
+        raw.z = f32x2_to_bf16x2(v[4], v[5]);
+        raw.w = f32x2_to_bf16x2(v[6], v[7]);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) = raw;
+    } else {
+        const float4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+        *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = a;
+        *reinterpret_cast<float4*>(static_cast<float*>(base) + idx + 4) = b;
+    }
+}
+
+template <int ACT, int OUT, int DV>
+__global__ __launch_bounds__(256) void gated_rmsnorm_kernel(NormParams p)
+{
+    constexpr int LPR = DV / 8;     // lanes per row
+    constexpr int RPW = 64 / LPR;   // rows per wave
+    const int lane = threadIdx.x & 63;
+    const long long total = static_cast<long long>(p.L) * p.B * p.T * p.HV;
+    const long long row = (static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+    const int col = (lane % LPR) * 8;
+    // a lane past the last row computes on the last row and stores nothing,
+    // so that every lane of a row group takes part in the reduction
+    const long long r = row < total ? row : total - 1;
+    const int b = static_cast<int>((r / (static_cast<long long>(p.T) * p.HV)) % p.B);
+    const int l = static_cast<int>(r / (static_cast<long long>(p.B) * p.T * p.HV));
+    const bool store = row < total && (!p.active || p.active[b] != 0);
+    const size_t base = static_cast<size_t>(r) * DV + col;
+
+    float ov[8], zv[8], wv[8];
+    load8<OUT>(p.o, base, ov);
+    load8<ACT>(p.z, base, zv);
+    load8<ACT>(p.w, static_cast<size_t>(l) * DV + col, wv);
+    float ss = ov[0] * ov[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) ss = fmaf(ov[i], ov[i], ss);
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    const float rn = 1.0f / sqrtf(ss / static_cast<float>(DV) + p.eps);
+    float yv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) yv[i] = ov[i] * rn * wv[i] * silu(zv[i]);
+    if (store) store8<OUT>(p.y, base, yv);
+}
+
+template <int DV>
+hipError_t launch_dv(const NormParams& p, long long total, hipStream_t s)
+{
+    constexpr int RPW = 64 / (DV / 8);
+    const long long waves = (total + RPW - 1) / RPW;
+    const long long blocks = (waves + 3) / 4;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (p.act == ACT_BF16) {
+        if (p.out == ACT_BF16) hipLaunchKernelGGL((gated_rmsnorm_kernel<ACT_BF16, ACT_BF16, DV>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gated_rmsnorm_kernel<ACT_BF16, ACT_F32, DV>), grid, dim3(256), 0, s, p);
+    } else {
+        if (p.out == ACT_BF16) hipLaunchKernelGGL((gated_rmsnorm_kernel<ACT_F32, ACT_BF16, DV>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((gated_rmsnorm_kernel<ACT_F32, ACT_F32, DV>), grid, dim3(256), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_gated_rmsnorm(const NormParams& p, hipStream_t s)
 {
     const long long total = static_cast<long long>(p.L) * p.B * p.T * p.HV;
-    const long long blocks = (total + 3) / 4;
-    if (total <= 0 || blocks > 0x7fffffffLL || p.DV > 128) return hipErrorInvalidConfiguration;
+    if (total <= 0) return hipErrorInvalidConfiguration;
     clear_stale_error();
-    const dim3 grid(static_cast<unsigned>(blocks));
-    if (p.act == ACT_BF16) {
-        if (p.out == ACT_BF16) hipLaunchKernelGGL((gated_rmsnorm_kernel<ACT_BF16, ACT_BF16>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((gated_rmsnorm_kernel<ACT_BF16, ACT_F32>), grid, dim3(256), 0, s, p);
-    } else {
-        if (p.out == ACT_BF16) hipLaunchKernelGGL((gated_rmsnorm_kernel<ACT_F32, ACT_BF16>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((gated_rmsnorm_kernel<ACT_F32, ACT_F32>), grid, dim3(256), 0, s, p);
+    switch (p.DV) {
+    case 16: return launch_dv<16>(p, total, s);
+    case 32: return launch_dv<32>(p, total, s);
+    case 64: return launch_dv<64>(p, total, s);
+    case 128: return launch_dv<128>(p, total, s);
+    default: return hipErrorInvalidConfiguration;
     }
-    return hipGetLastError();
 }
 
 }  // namespace gdn

@@ -30,7 +30,7 @@ def inputs(sh, seed):
     return o, z, w
 
 
-@pytest.mark.parametrize("DV,out", [(128, "f32"), (64, "f32"), (16, "f32"), (128, "bf16")])
+@pytest.mark.parametrize("DV,out", [(128, "f32"), (64, "f32"), (32, "f32"), (16, "f32"), (128, "bf16")])
 def test_gated_rmsnorm_matches_oracle(DV, out):
     torch = torch_mod()
     sh = W.COHORT.with_(L=2, DV=DV, DK=128 if DV == 128 else DV, out=out)
@@ -54,6 +54,27 @@ def test_gated_rmsnorm_matches_oracle(DV, out):
     else:
         r = W.bf16_round(ref[:, a].astype(np.float32)).astype(np.float64)
         assert np.all(np.abs(yg[:, a] - r) <= np.abs(r) * 2 ** -7 + 1e-30)
+
+
+@pytest.mark.parametrize("DV", [16, 32, 64, 128])
+def test_gated_rmsnorm_ragged_row_count(DV):
+    """45 (layer, row, token, head) rows: not a multiple of the rows a wave
+    takes at any d_v, so the last wave is partly past the end; rows 1 and 3
+    inactive."""
+    torch = torch_mod()
+    sh = W.Shape("pfn", L=1, B=5, T=3, HV=3, HK=1, DK=16, DV=DV, S=1, out="f32")
+    o, z, w = inputs(sh, 8200 + DV)
+    active = np.array([1, 0, 1, 0, 1], np.uint8)
+    bd, od = dims_pair(sh)
+    y = torch.full(o.shape, float("nan"), device="cuda")
+    B().gdn_gated_rmsnorm(bd, dev(o, torch.float32), dev(z, torch.bfloat16), dev(w, torch.bfloat16), y,
+                          eps=1e-6, active=dev(active))
+    torch.cuda.synchronize()
+    ref = oracle.gated_rmsnorm(od, o, z, w, eps=float(np.float32(1e-6)), active=active)
+    yg = host(y).astype(np.float64)
+    a = active.astype(bool)
+    assert np.all(np.isnan(yg[:, ~a]))
+    assert block_err(yg[:, a], ref[:, a], (-1,)) <= 1e-5
 
 
 def test_gated_rmsnorm_in_place_after_verify():
