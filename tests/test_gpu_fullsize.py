@@ -1,6 +1,7 @@
 """Parity at the benchmark's full sizes and launch configuration: the B8/T2
 cohort over 30 layer pools in one grouped verify, one grouped commit, the
-fused commit + verify of the next cycle, and the B8/T4 rewind over 30 layers.
+fused commit + verify of the next cycle, the verify with the fused gated
+RMSNorm, and the B8/T4 rewind over 30 layers.
 The oracle recomputes sampled layers (0, 14, 29) one by one; every other
 layer is checked by properties that hold at any size (inactive rows and the
 snapshot slot untouched, finite outputs).  Inputs are drawn on the device
@@ -169,3 +170,48 @@ def test_rewind_b8_t4_thirty_layers():
                 assert np.array_equal(st_l[:, b], inp["state"][:, b])
             else:
                 assert state_err(st_l[:, b, c0], st_ref[:, b, c0]) <= 2e-3
+
+
+def test_cohort_thirty_layers_verify_with_fused_gated_norm():
+    """gdn_verify_gated_norm over the 30 layer pools (the bench's fused-norm
+    launch): candidates bit-equal to the plain grouped verify on every layer,
+    y against the oracle's verify followed by its gated RMSNorm on the sampled
+    layers, inactive rows untouched."""
+    torch = torch_mod()
+    sh = W.COHORT
+    t = pools(sh, 9201)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9202)
+    z = torch.randn((L_FULL, sh.B, sh.T, sh.HV, sh.DV), generator=gen, device="cuda").to(torch.bfloat16)
+    w = (1.0 + 0.1 * torch.randn((L_FULL, sh.DV), generator=gen, device="cuda")).to(torch.bfloat16)
+    act = np.ones(sh.B, np.uint8)
+    act[list(sh.inactive)] = 0
+    act_d = torch.from_numpy(act).cuda()
+    before = {l: layer(t, l) for l in SAMPLED}
+    bd, _ = dims_pair(sh, L=L_FULL)
+    _, od1 = dims_pair(sh, L=1)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st_plain = t["state"].clone()
+    o = torch.full((L_FULL, sh.B, sh.T, sh.HV, sh.DV), float("nan"), device="cuda")
+    B().gdn_verify(bd, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"], st_plain,
+                   t["cur"], o, act_d, err)
+    y = torch.full_like(o, float("nan"))
+    B().gdn_verify_gated_norm(bd, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
+                              t["state"], t["cur"], z, w, y, eps=1e-6, active=act_d, err=err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    assert torch.equal(t["state"], st_plain)
+    y_h = host(y).astype(np.float64)
+    a = act.astype(bool)
+    assert np.all(np.isfinite(y_h[:, a])) and np.all(np.isnan(y_h[:, ~a]))
+    z_h, w_h = host(z), host(w)
+    for l in SAMPLED:
+        inp = before[l]
+        _, o_ref, e = oracle.verify(od1, inp["x"], inp["conv_w"], None, inp["conv_state"],
+                                    inp["g"], inp["beta"], inp["state"], inp["cur"], act)
+        assert e == 0
+        y_ref = oracle.gated_rmsnorm(od1, o_ref, z_h[l:l + 1], w_h[l:l + 1],
+                                     eps=float(np.float32(1e-6)), active=act)
+        num = np.max(np.abs(y_h[l:l + 1][:, a] - y_ref[:, a]), axis=-1)
+        den = np.maximum(np.max(np.abs(y_ref[:, a]), axis=-1), 1e-30)
+        assert np.max(num / den) <= 2e-3
