@@ -161,6 +161,18 @@ __device__ __forceinline__ float load_act(const void* base, size_t idx)
     else return static_cast<const float*>(base)[idx];
 }
 
+// Workgroup barrier over LDS only: waits for this wave's LDS accesses, then
+// for the other waves.  __syncthreads() also fences global memory, which on
+// this architecture means waiting for every global load and store the wave
+// has in flight (one counter covers both), so a prefetch issued before the
+// barrier is waited for there and stores just issued stall the next phase.
+// For kernels whose workgroups never read global memory they wrote
+// themselves, LDS is all a barrier has to order.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
 }  // namespace gdn

@@ -277,7 +277,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
         Gs[lane] = gv * 1.4426950408889634f;   // log2(e): decays below are exp2 of differences
         Bs[lane] = lane < n ? braw : 0.f;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- K K^T and K Q^T: rows i (all tiles), columns r (tile w) ----
     f32x4 kk[4], kq[4];
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
             for (int ks = 0; ks < 2; ++ks) Vf[nt][ks][lane] = frag_from_c(d4[2 * ks], d4[2 * ks + 1]);
         }
     }
-    __syncthreads();   // K and V rows are dead from here on (region 1 becomes A and T)
+    lds_barrier();   // K and V rows are dead from here on (region 1 becomes A and T)
 
     // ---- A (fp32, LDS), P = scale lower_incl(E o Q^K^T) (split A-frags), per-token vectors ----
     {
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
                     *reinterpret_cast<f32x4*>(&Tf[rr * FP + 16 * qb + 4 * e]) = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    __syncthreads();   // A complete
+    lds_barrier();   // A complete
 
     // ---- T = (I + A)^-1 on fp32 MFMA, 16x16 blocks by recursive doubling ----
     {
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
             __builtin_amdgcn_wave_barrier();
         }
     }
-    __syncthreads();
+    lds_barrier();
     // off-diagonal 16x16 blocks of the two 32x32 halves: T10 = -D1 A10 D0, T32 = -D3 A32 D2
     if (w == 1 || w == 3) {
         const int b = 16 * (w - 1);   // column block of the pair
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
         const f32x4 t = blk_mul<FP, SP>(Tf, b + 16, b + 16, S0, 0, 0, f32x4{0.f, 0.f, 0.f, 0.f}, fr, gq);
         blk_store<FP>(Tf, b + 16, b, t, -1.f, fr, gq);
     }
-    __syncthreads();
+    lds_barrier();
     // lower-left 32x32 quadrant: X = A[32:64, 0:32] T[0:32, 0:32], then T21 = -T22 X.
     // Block (pr, pc) of X lives in Scr[pr][pc].
     {
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
             xa = blk_mul<FP, FP>(Af, 32 + 16 * pr, 16 * kb, Tf, 16 * kb, 16 * pc, xa, fr, gq);
         blk_store<SP>(&Scr[pr][pc][0][0], 0, 0, xa, 1.f, fr, gq);
     }
-    __syncthreads();
+    lds_barrier();
     {
         const int pr = w >> 1, pc = w & 1;
         f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
             t = blk_mul<FP, SP>(Tf, 32 + 16 * pr, 32 + 16 * kb, &Scr[kb][pc][0][0], 0, 0, t, fr, gq);
         blk_store<FP>(Tf, 32 + 16 * pr, 16 * pc, t, -1.f, fr, gq);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- U~ = T diag(beta) V (split T) and W~^T = K^T (T diag(beta gamma / |k|))^T ----
     // Both read row r_me of T over the permuted token order.
@@ -500,7 +500,8 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
 //    operands themselves.
 // One barrier per chunk hands a ring slot from the state wave to the output
 // waves; they finish reading slot c%2 before they reach the next barrier,
-// after which the state wave may overwrite it.
+// after which the state wave may overwrite it.  The barrier orders LDS only,
+// so the prefetches issued just before it stay in flight across it.
 //
 // Every load and store goes through a buffer resource whose base moves with
 // the chunk, so a per-access address is a lane-constant VGPR plus constants
@@ -746,16 +747,16 @@ __device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK>& ring,
     for (; c + 2 <= NC; c += 2) {
         rb = chunk_res<DK, DV, OUT>(p, recs, recs_kq, c + 1, len, lb, hv);
         out_load<DK, DV, TA, TB>(fb, rb.rec, rb.kq, lane16, vq16);
-        __syncthreads();
+        lds_barrier();
         out_chunk<DK, DV, OUT, TA, TB>(fa, ring, c, ra.o, vo, lane);
         const int c2 = min(c + 2, NC - 1);
         ra = chunk_res<DK, DV, OUT>(p, recs, recs_kq, c2, len, lb, hv);
         out_load<DK, DV, TA, TB>(fa, ra.rec, ra.kq, lane16, vq16);
-        __syncthreads();
+        lds_barrier();
         out_chunk<DK, DV, OUT, TA, TB>(fb, ring, c + 1, rb.o, vo, lane);
     }
     if (c < NC) {
-        __syncthreads();
+        lds_barrier();
         out_chunk<DK, DV, OUT, TA, TB>(fa, ring, c, ra.o, vo, lane);
     }
 }
@@ -828,14 +829,14 @@ __global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
         for (; c + 2 <= NCr; c += 2) {
             k_load<DK, DV>(fb, rec_rsrc(c + 1), kq_rsrc(c + 1), lane16, vq16, cs);
             state_chunk<DK, DV>(wf, fa, rec_rsrc(c + 1), h, ring, c, lane);
-            __syncthreads();
+            lds_barrier();
             k_load<DK, DV>(fa, rec_rsrc(c + 2), kq_rsrc(c + 2), lane16, vq16, cs);
             state_chunk<DK, DV>(wf, fb, rec_rsrc(c + 2), h, ring, c + 1, lane);
-            __syncthreads();
+            lds_barrier();
         }
         if (c < NCr) {
             state_chunk<DK, DV>(wf, fa, rec_rsrc(c), h, ring, c, lane);
-            __syncthreads();
+            lds_barrier();
         }
 #pragma unroll
         for (int a = 0; a < DK / 16; ++a)

@@ -269,7 +269,7 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
 #pragma unroll
                 for (int c = 0; c < 4; ++c) gzw[wid][t][j4 * 4 + c] = nw[c] * silu(zv[t][c]);
     }
-    __syncthreads();
+    lds_barrier();
 
     const bool l2 = (p.flags & FLAG_L2) != 0;
     for (int t = 0; t < nsteps; ++t) {
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
 #pragma unroll
                 for (int off = 1; off < JL; off <<= 1) ss += __shfl_xor(ss, off, 64);
                 if (lane == 0) ssq[t][wid] = ss;
-                __syncthreads();
+                lds_barrier();
                 float tot = ssq[t][0];
 #pragma unroll
                 for (int w = 1; w < NW; ++w) tot += ssq[t][w];
