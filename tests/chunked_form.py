@@ -18,9 +18,11 @@ Networks", ICLR 2025.)  q and k are L2-normalised per token first.  The
 chunked recurrence differs from the sequential one only in rounding ("MTP
 inference: review and commit structure", Verification and limits).
 
-`bf16` selects emulated bf16 MFMA operands: every product whose operands are
-not exact bf16 inputs splits them into hi + lo bf16 parts as the kernels do.
-This module shares no code with the oracle or the HIP path.
+`bf16` selects emulated bf16 MFMA operands with fp32 accumulation modelled in
+float64: each product's operands are exact inputs ('x'), split into hi + lo
+bf16 parts ('s', three products, lo x lo dropped) or rounded to bf16 once
+('b').  KERNEL_PLAN is the plan the prefill kernels use; `plan` overrides
+entries of it.  This module shares no code with the oracle or the HIP path.
 """
 from __future__ import annotations
 
@@ -66,7 +68,17 @@ def _mm(a, b, plan):
     return aa @ bb
 
 
-def chunked_head(q, k, v, g, beta, H0, chunk=64, scale=1.0, l2=True, eps=1e-6, bf16=False):
+# Operand treatment per product, as in the prefill kernels: K K^T and Q K^T
+# take the exact bf16 inputs; T diag(beta) is split for U~ and T diag(beta
+# gamma / |k|) rounded once for W~; W~ and H are each rounded once inside
+# W~ H; H is split inside Q H; P and U are split inside P U; diag(s) U is
+# split inside K^T diag(s) U.
+KERNEL_PLAN = dict(kk=("x", "x"), qk=("x", "x"), tv=("s", "x"), tk=("b", "x"), wh=("b", "b"),
+                   qh=("x", "s"), pu=("s", "s"), ku=("x", "s"))
+
+
+def chunked_head(q, k, v, g, beta, H0, chunk=64, scale=1.0, l2=True, eps=1e-6, bf16=False,
+                 plan=None):
     """q, k (T, dk) raw; v (T, dv); g, beta (T,); H0 (dk, dv).
     Returns (H_T, O)."""
     q = np.asarray(q, np.float64)
@@ -77,8 +89,7 @@ def chunked_head(q, k, v, g, beta, H0, chunk=64, scale=1.0, l2=True, eps=1e-6, b
     T = q.shape[0]
     H = np.array(H0, np.float64)
     O = np.zeros((T, v.shape[1]))
-    P = {} if not bf16 else dict(kk=("x", "x"), qk=("x", "x"), tv=("s", "x"), tk=("s", "x"),
-                                 wh=("s", "s"), qh=("x", "s"), pu=("s", "s"), ku=("x", "s"))
+    P = {} if not bf16 else dict(KERNEL_PLAN, **(plan or {}))
     for c0 in range(0, T, chunk):
         sl = slice(c0, min(c0 + chunk, T))
         n = sl.stop - sl.start
