@@ -399,6 +399,16 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
 // up to T steps between its single read and single write of the slice and
 // needs the other waves to cover that, so it runs uncapped.
 constexpr int kVerifyWgPerCU = 4;   // one wave per SIMD
+// A verify grid many rounds deep (the 30-layer B8/T2 cohort: 30,720
+// workgroups, 30 rounds at four per CU) runs faster at five per CU once it is
+// streaming: in the decode loop (verify + commit replayed from a HIP graph)
+// 215-220 us per step against 227-236 us at four and 216-217 us at six, and
+// 203-205 us against 206-208 us for back-to-back verify launches (three
+// interleaved runs of each on one MI355X).  Short grids keep four: the solo
+// B1/T3 launch over 30 layers (3,840 workgroups) takes 56.9 us at four
+// against 58.7 us at five and 58.9 us at six.
+constexpr int kVerifyWgPerCULong = 5;
+constexpr int kVerifyLongRounds = 8;   // rounds at four per CU beyond which the long cap applies
 // Verify with the fused norm runs the NS waves of a head as one workgroup
 // with a barrier per token, so a wave stalls for its siblings; two such
 // workgroups per CU (two waves per SIMD) cover that (B8/T2 cohort, 30
@@ -407,6 +417,23 @@ constexpr int kVerifyWgPerCU = 4;   // one wave per SIMD
 constexpr int kVerifyNormWgPerCU = 2;
 constexpr int kRewindWgPerCU = 0;   // no cap
 constexpr int kLazyWgPerCU = 0;     // no cap (replay steps between read and write)
+
+// Compute units of the current device, queried once per device (0 if unknown).
+static int device_cus()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            clear_stale_error();
+            return 0;
+        }
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 static size_t occupancy_lds_bytes(size_t static_bytes, int wg_per_cu)
 {
@@ -476,6 +503,11 @@ static hipError_t launch_rec(RecParams p, hipStream_t s)
     if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     int cap = p.mode == REC_VERIFY ? kVerifyWgPerCU : p.mode == REC_LAZY ? kLazyWgPerCU : kRewindWgPerCU;
     if (norm && nw > 1 && p.mode == REC_VERIFY) cap = kVerifyNormWgPerCU;
+    if (p.mode == REC_VERIFY && !norm) {
+        const int cus = device_cus();
+        if (cus > 0 && blocks > static_cast<long long>(kVerifyLongRounds) * kVerifyWgPerCU * cus)
+            cap = kVerifyWgPerCULong;
+    }
     const dim3 grid(static_cast<unsigned>(blocks));
     clear_stale_error();
     if (lazy) {
