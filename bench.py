@@ -149,6 +149,43 @@ def commit_bytes(sh, keep, active, L):
     return L * (n * 6 * sh.C * esz + sh.B * 9)
 
 
+def algorithmic_min_bytes(sh, keep, active, L):
+    """The fewest bytes one verify + commit cycle can move: per active (layer,
+    row) one read of its fp32 state, the window inputs x, conv cache, g and
+    beta, and the fp32 outputs; per committing (layer, row) one write of its
+    state and of its new conv cache; per layer the conv weights.  The
+    verify + commit split writes T candidates instead of one committed state."""
+    esz = 2 if sh.act == "bf16" else 4
+    tile = sh.HV * sh.DK * sh.DV * 4
+    n_act = int(np.sum(active > 0))
+    n_com = int(np.sum((keep > 0) & (active > 0)))
+    per_act = tile + (sh.T + 3) * sh.C * esz + 2 * sh.T * sh.HV * esz + sh.T * sh.HV * sh.DV * 4
+    per_com = tile + 3 * sh.C * esz
+    return L * (n_act * per_act + n_com * per_com + sh.C * 4 * esz)
+
+
+def stream_copy_gbs(torch):
+    """Device-to-device copy rate of a 1 GiB buffer (read + write bytes per
+    second), the practical ceiling of a kernel that streams memory."""
+    n = 1 << 28
+    a = torch.empty(n, device="cuda")
+    a.fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    tm = Timer(torch)
+    e0 = tm.ev()
+    reps = 5
+    for _ in range(reps):
+        b.copy_(a)
+    e1 = tm.ev()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 4 * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def headline(torch, gb, W, args):
     """The headline cycle: one grouped verify over the 30 layer pools, then one
     grouped commit with a fresh device keep vector.  The K timed cycles are
@@ -200,12 +237,16 @@ def headline(torch, gb, W, args):
     n_act = int(act_rows.sum())
     vb = verify_bytes(sh, n_act, L_POOL)
     cb = float(np.mean([commit_bytes(sh, keeps[i], act_rows, L_POOL) for i in range(args.warmup, n)]))
+    amin = float(np.mean([algorithmic_min_bytes(sh, keeps[i], act_rows, L_POOL)
+                          for i in range(args.warmup, n)]))
     ms_step = total_ms / args.steps
     rows_heads = L_POOL * sh.B * sh.HV
     res = dict(ms_per_step=ms_step, value=rows_heads * args.steps / (total_ms / 1e3),
                verify_ms=verify_ms, verify_bytes=vb, commit_bytes=cb,
                verify_gbs=vb / (verify_ms / 1e3) / 1e9,
                cycle_gbs=(vb + cb) / (ms_step / 1e3) / 1e9,
+               algorithmic_min_bytes_per_cycle=amin,
+               algorithmic_min_gbs=amin / (ms_step / 1e3) / 1e9,
                active_rows_heads_per_s=L_POOL * n_act * sh.HV * args.steps / (total_ms / 1e3))
     del t, graph
     torch.cuda.empty_cache()
@@ -748,6 +789,8 @@ def main():
         log("bench: cpu baseline (oracle)")
         cpu = cpu_baseline(W)
     vb = h["verify_bytes"]
+    log("bench: device copy rate")
+    copy_gbs = stream_copy_gbs(torch)
     rec = {
         "metric": "GDN verify+commit rows*heads/s (B8,T2,32 heads) + achieved HBM GB/s vs peak",
         "value": h["value"],
@@ -771,8 +814,12 @@ def main():
                      "frac": h["verify_gbs"] / HBM_PEAK_GBS,
                      "traffic": counted_traffic("recurrent_kernel_verify_b8_t2_l30"),
                      "algorithmic_bytes_per_launch": vb,
-                     "avg_launch_ms": h["verify_ms"]},
+                     "avg_launch_ms": h["verify_ms"],
+                     "stream_copy_gbs": copy_gbs,
+                     "frac_of_stream": h["verify_gbs"] / copy_gbs},
         "cycle_gbs": h["cycle_gbs"],
+        "algorithmic_min_bytes_per_cycle": h["algorithmic_min_bytes_per_cycle"],
+        "algorithmic_min_gbs": h["algorithmic_min_gbs"],
         "active_rows_heads_per_s": h["active_rows_heads_per_s"],
         "cpu_baseline": cpu,
         "extra": extra,
