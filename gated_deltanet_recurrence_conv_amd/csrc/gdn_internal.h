@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace gdn {
 
 enum { ACT_F32 = 0, ACT_BF16 = 1 };
@@ -79,6 +81,24 @@ struct ConvParams {
 // Drops an error a previous runtime call may have left behind, so that the
 // status read right after a launch belongs to that launch.
 inline void clear_stale_error() { (void)hipGetLastError(); }
+
+// Compute units of the current device, queried once per device (0 if the
+// query fails; callers then keep their default launch shape).
+inline int device_cus()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            clear_stale_error();
+            return 0;
+        }
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 hipError_t launch_recurrent(const RecParams& p, int DK, int DV, hipStream_t s);
 hipError_t launch_window(const WinParams& p, hipStream_t s);

@@ -657,7 +657,7 @@ __device__ __forceinline__ void out_load(OutFrags<DK, DV>& f, rsrc_t rrec, rsrc_
 
 template <int DK, int DV, int OUT, int TA, int TB>
 __device__ __forceinline__ void out_chunk(const OutFrags<DK, DV>& f, const Ring<DK>& ring, int c, rsrc_t ro,
-                                          const int (&vo)[2][4], int lane)
+                                          const int (&vo)[2][4], int coff, int lane)
 {
     constexpr int KS = DK / 32;
     const int slot = c & 1;
@@ -697,9 +697,9 @@ __device__ __forceinline__ void out_chunk(const OutFrags<DK, DV>& f, const Ring<
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if constexpr (OUT == ACT_BF16)
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(o[j]), ro, vo[i][j], 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(o[j]), ro, vo[i][j] + coff, 0, 0);
             else
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[j]), ro, vo[i][j], 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[j]), ro, vo[i][j] + coff, 0, 0);
         }
     }
 }
@@ -726,9 +726,12 @@ __device__ __forceinline__ ChunkRes chunk_res(const PrefillParams& p, const char
     return r;
 }
 
-template <int DK, int DV, int OUT, int TA, int TB>
-__device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK>& ring, const char* recs, const char* recs_kq,
-                                         int NC, int len, int lb, int hv, int cs, int lane)
+// Output wave of a workgroup carrying SL column slices (16 SL columns from
+// column 16 SL cs): the Q, P and scaling operands are the same for every
+// slice of the head, so they are loaded once and used SL times.
+template <int DK, int DV, int OUT, int TA, int TB, int SL>
+__device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK> (&ring)[SL], const char* recs,
+                                         const char* recs_kq, int NC, int len, int lb, int hv, int cs, int lane)
 {
     constexpr int OSZ = OUT == ACT_BF16 ? 2 : 4;
     const int fr = lane & 15, gq = lane >> 4;
@@ -738,8 +741,12 @@ __device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK>& ring,
     for (int i = 0; i < 2; ++i) {
         const int tb = i ? TB : TA;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vo[i][j] = ((16 * tb + 4 * gq + j) * p.HV * DV + 16 * cs + fr) * OSZ;
+        for (int j = 0; j < 4; ++j) vo[i][j] = ((16 * tb + 4 * gq + j) * p.HV * DV + 16 * SL * cs + fr) * OSZ;
     }
+    auto chunk_out = [&](const OutFrags<DK, DV>& f, int cc, rsrc_t ro) {
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) out_chunk<DK, DV, OUT, TA, TB>(f, ring[sl], cc, ro, vo, 16 * sl * OSZ, lane);
+    };
     OutFrags<DK, DV> fa, fb;
     ChunkRes ra = chunk_res<DK, DV, OUT>(p, recs, recs_kq, 0, len, lb, hv), rb;
     out_load<DK, DV, TA, TB>(fa, ra.rec, ra.kq, lane16, vq16);
@@ -748,30 +755,31 @@ __device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK>& ring,
         rb = chunk_res<DK, DV, OUT>(p, recs, recs_kq, c + 1, len, lb, hv);
         out_load<DK, DV, TA, TB>(fb, rb.rec, rb.kq, lane16, vq16);
         lds_barrier();
-        out_chunk<DK, DV, OUT, TA, TB>(fa, ring, c, ra.o, vo, lane);
+        chunk_out(fa, c, ra.o);
         const int c2 = min(c + 2, NC - 1);
         ra = chunk_res<DK, DV, OUT>(p, recs, recs_kq, c2, len, lb, hv);
         out_load<DK, DV, TA, TB>(fa, ra.rec, ra.kq, lane16, vq16);
         lds_barrier();
-        out_chunk<DK, DV, OUT, TA, TB>(fb, ring, c + 1, rb.o, vo, lane);
+        chunk_out(fb, c + 1, rb.o);
     }
     if (c < NC) {
         lds_barrier();
-        out_chunk<DK, DV, OUT, TA, TB>(fa, ring, c, ra.o, vo, lane);
+        chunk_out(fa, c, ra.o);
     }
 }
 
-template <int DK, int DV, int OUT>
-__global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
+template <int DK, int DV, int OUT, int SL>
+__global__ __launch_bounds__(64 * (SL + 2)) void prefill_scan_kernel(PrefillParams p)
 {
     using R = Rec<DK, DV>;
-    __shared__ __align__(16) Ring<DK> ring;
+    static_assert(SL >= 1 && (DV / 16) % SL == 0, "a workgroup's slices must divide d_v");
+    __shared__ __align__(16) Ring<DK> ring[SL];
 
     // ---- block -> (layer*row, qk head, value head, column slice), XCD-aware:
     // workgroups go round-robin over the 8 XCDs, so the index is remapped to
     // put every slice of the value heads of one qk head on one XCD, where
     // they share the chunk records and q rows through its L2.
-    constexpr int NS = DV / 16;
+    constexpr int NS = DV / 16 / SL;   // workgroups per value head
     const int gsz = p.HV / p.HK;
     const int per_group = gsz * NS;
     const int bid = blockIdx.x;
@@ -803,11 +811,12 @@ __global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
     const char* recs_kq = static_cast<const char*>(p.ws) + (static_cast<size_t>(lb) * p.HV + m * gsz) * NC * R::BYTES;
     const int NCr = (len + CH - 1) / CH;   // chunks of this row's prompt
 
-    if (w == 0) {
-        // ---- state wave ----
+    if (w < SL) {
+        // ---- state wave of column slice SL cs + w ----
+        const int sc = SL * cs + w;
         const int fr = lane & 15, fq = (lane >> 4) * 4;
         const int lane16 = lane * 16, vq16 = (lane >> 4) * 16;
-        const int col = 16 * cs + fr;
+        const int col = 16 * sc + fr;
         float* st = p.state + ((static_cast<size_t>(lb) * p.S + slot) * p.HV + hv) * DK * DV;
         f32x4 h[DK / 16];
 #pragma unroll
@@ -824,28 +833,28 @@ __global__ __launch_bounds__(192) void prefill_scan_kernel(PrefillParams p)
         WFrags<DK> wf;
         KFrags<DK, DV> fa, fb;
         w_load<DK, DV>(wf, rec_rsrc(0), lane16);
-        k_load<DK, DV>(fa, rec_rsrc(0), kq_rsrc(0), lane16, vq16, cs);
+        k_load<DK, DV>(fa, rec_rsrc(0), kq_rsrc(0), lane16, vq16, sc);
         int c = 0;
         for (; c + 2 <= NCr; c += 2) {
-            k_load<DK, DV>(fb, rec_rsrc(c + 1), kq_rsrc(c + 1), lane16, vq16, cs);
-            state_chunk<DK, DV>(wf, fa, rec_rsrc(c + 1), h, ring, c, lane);
+            k_load<DK, DV>(fb, rec_rsrc(c + 1), kq_rsrc(c + 1), lane16, vq16, sc);
+            state_chunk<DK, DV>(wf, fa, rec_rsrc(c + 1), h, ring[w], c, lane);
             lds_barrier();
-            k_load<DK, DV>(fa, rec_rsrc(c + 2), kq_rsrc(c + 2), lane16, vq16, cs);
-            state_chunk<DK, DV>(wf, fb, rec_rsrc(c + 2), h, ring, c + 1, lane);
+            k_load<DK, DV>(fa, rec_rsrc(c + 2), kq_rsrc(c + 2), lane16, vq16, sc);
+            state_chunk<DK, DV>(wf, fb, rec_rsrc(c + 2), h, ring[w], c + 1, lane);
             lds_barrier();
         }
         if (c < NCr) {
-            state_chunk<DK, DV>(wf, fa, rec_rsrc(c), h, ring, c, lane);
+            state_chunk<DK, DV>(wf, fa, rec_rsrc(c), h, ring[w], c, lane);
             lds_barrier();
         }
 #pragma unroll
         for (int a = 0; a < DK / 16; ++a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) st[(16 * a + fq + j) * DV + col] = h[a][j];
-    } else if (w == 1) {
-        out_wave<DK, DV, OUT, 0, 3>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
+    } else if (w == SL) {
+        out_wave<DK, DV, OUT, 0, 3, SL>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
     } else {
-        out_wave<DK, DV, OUT, 1, 2>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
+        out_wave<DK, DV, OUT, 1, 2, SL>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
     }
 }
 
@@ -860,15 +869,29 @@ hipError_t launch_pf(const PrefillParams& p, hipStream_t s)
                        dim3(NTHR), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // One 16-column slice per workgroup while the grid fits the GPU in one
+    // round (the slice's chain sets the time); deeper grids put two slices
+    // of a head in each workgroup, whose output waves serve both.
     const long long groups = rows * p.HK;
-    const long long blocks = (groups + 7) / 8 * 8 * (p.HV / p.HK) * (DV / 16);
+    const long long blocks1 = (groups + 7) / 8 * 8 * (p.HV / p.HK) * (DV / 16);
+    const int cus = device_cus();
+    const bool two = DV >= 32 && cus > 0 && blocks1 > cus;
+    const long long blocks = two ? blocks1 / 2 : blocks1;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    if (p.out == ACT_BF16)
-        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16>), dim3(static_cast<unsigned>(blocks)), dim3(192),
-                           0, s, p);
-    else
-        hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32>), dim3(static_cast<unsigned>(blocks)), dim3(192),
-                           0, s, p);
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if constexpr (DV >= 32) {
+        if (two) {
+            if (p.out == ACT_BF16)
+                hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16, 2>), grid, dim3(256), 0, s, p);
+            else
+                hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32, 2>), grid, dim3(256), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    {
+        if (p.out == ACT_BF16) hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16, 1>), grid, dim3(192), 0, s, p);
+        else hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32, 1>), grid, dim3(192), 0, s, p);
+    }
     return hipGetLastError();
 }
 

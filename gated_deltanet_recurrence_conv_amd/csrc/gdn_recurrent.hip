@@ -418,23 +418,6 @@ constexpr int kVerifyNormWgPerCU = 2;
 constexpr int kRewindWgPerCU = 0;   // no cap
 constexpr int kLazyWgPerCU = 0;     // no cap (replay steps between read and write)
 
-// Compute units of the current device, queried once per device (0 if unknown).
-static int device_cus()
-{
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
-            clear_stale_error();
-            return 0;
-        }
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 static size_t occupancy_lds_bytes(size_t static_bytes, int wg_per_cu)
 {
     if (wg_per_cu <= 0) return 0;

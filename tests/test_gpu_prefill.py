@@ -292,3 +292,48 @@ def test_prefill_ragged_bad_length_reported():
         assert np.all(np.isnan(o_g[:, b]))
     assert not np.array_equal(st_g[:, 0], inp["state"][:, 0])
     assert np.all(np.isfinite(o_g[:, 0, :50])) and np.all(np.isnan(o_g[:, 0, 50:]))
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_prefill_two_slice_workgroups_equal_single_row_calls(out):
+    """Four ragged prompts at the Qwen head shape (32 value / 16 qk heads,
+    d = 128): 1,024 one-slice scan workgroups, more than the GPU holds at
+    once, so the scan runs two column slices per workgroup.  Each row equals
+    a single-row call (one slice per workgroup) bit for bit, and the
+    token-sequential oracle within 2e-3."""
+    torch = torch_mod()
+    lengths = np.array([200, 64, 1, 131], np.int32)
+    T = int(lengths.max())
+    sh = W.Shape("pf2", L=1, B=4, T=T, HV=32, HK=16, DK=128, DV=128, S=2)
+    inp = W.prefill_inputs(sh, seed=3700)
+    inp["state"] = W.random_state(sh, seed=3701)
+    inp["cur"] = np.array([[1, 0, 1, 0]], np.int32)
+    A = act_dtype(sh.act)
+    d, _ = dims_pair(sh, out=out)
+    st = dev(inp["state"], torch.float32)
+    o = torch.full((1, sh.B, T, sh.HV, sh.DV), float("nan"), device="cuda", dtype=act_dtype(out))
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(B().gdn_workspace_size(d), dtype=torch.uint8, device="cuda")
+    B().gdn_prefill_ragged(d, dev(inp["y"], A), dev(inp["g"], A), dev(inp["beta"], A), st,
+                           dev(inp["cur"], torch.int32), o, dev(lengths), 64, ws, err)
+    torch.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    st_g, o_g = host(st), host(o)
+    for b, n in enumerate(lengths):
+        assert np.all(np.isnan(o_g[:, b, n:]))
+        one = sh.with_(B=1, T=int(n))
+        row = {k: np.ascontiguousarray(inp[k][:, b:b + 1, :n]) for k in ("y", "g", "beta")}
+        row["state"] = np.ascontiguousarray(inp["state"][:, b:b + 1])
+        row["cur"] = np.ascontiguousarray(inp["cur"][:, b:b + 1])
+        st1, o1 = gpu_prefill(one, row, out=out)
+        assert np.array_equal(st_g[:, b:b + 1], st1), b
+        assert np.array_equal(o_g[:, b:b + 1, :n], o1), b
+        st_r, o_r, e = oracle_prefill(one, row)
+        assert e == 0
+        c0 = int(inp["cur"][0, b])
+        assert state_err(st_g[:, b, c0], st_r[:, 0, c0]) <= 2e-3, b
+        if out == "f32":
+            assert out_err(o_g[:, b:b + 1, :n], o_r) <= 2e-3, b
+        else:   # the oracle's value rounded to bf16, within one more bf16 unit
+            assert out_err(o_g[:, b:b + 1, :n].astype(np.float64),
+                           W.bf16_round(o_r.astype(np.float32))) <= 2 ** -7, b
