@@ -521,10 +521,6 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, int voff, int soff)
 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
-__device__ __forceinline__ uint2 bload8(rsrc_t r, int voff, int soff)
-{
-    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
-}
 __device__ __forceinline__ f32x4 as_f4(const uint4& v)
 {
     return __builtin_bit_cast(f32x4, v);
