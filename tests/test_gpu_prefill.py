@@ -294,20 +294,23 @@ def test_prefill_ragged_bad_length_reported():
     assert np.all(np.isfinite(o_g[:, 0, :50])) and np.all(np.isnan(o_g[:, 0, 50:]))
 
 
-@pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_prefill_two_slice_workgroups_equal_single_row_calls(out):
-    """Four ragged prompts at the Qwen head shape (32 value / 16 qk heads,
-    d = 128): 1,024 one-slice scan workgroups, more than the GPU holds at
-    once, so the scan runs two column slices per workgroup.  Each row equals
-    a single-row call (one slice per workgroup) bit for bit, and the
+@pytest.mark.parametrize("DK,DV,lengths,out", [
+    (128, 128, (200, 64, 1, 131), "f32"), (128, 128, (200, 64, 1, 131), "bf16"),
+    (64, 64, (70, 128, 5, 64), "f32"), (32, 32, (90, 1, 64, 65, 3, 128, 40, 7), "f32")])
+def test_prefill_two_slice_workgroups_equal_single_row_calls(DK, DV, lengths, out):
+    """Ragged prompts at 32 value / 16 qk heads: 512 to 1,024 one-slice scan
+    workgroups, more than the GPU holds at once, so the scan runs two column
+    slices per workgroup.  Each row equals a single-row call (256 or fewer
+    workgroups: one slice per workgroup) bit for bit, and the
     token-sequential oracle within 2e-3."""
     torch = torch_mod()
-    lengths = np.array([200, 64, 1, 131], np.int32)
+    lengths = np.array(lengths, np.int32)
     T = int(lengths.max())
-    sh = W.Shape("pf2", L=1, B=4, T=T, HV=32, HK=16, DK=128, DV=128, S=2)
+    nb = len(lengths)
+    sh = W.Shape("pf2", L=1, B=nb, T=T, HV=32, HK=16, DK=DK, DV=DV, S=2)
     inp = W.prefill_inputs(sh, seed=3700)
     inp["state"] = W.random_state(sh, seed=3701)
-    inp["cur"] = np.array([[1, 0, 1, 0]], np.int32)
+    inp["cur"] = (np.arange(nb, dtype=np.int32) % 2)[None, :]
     A = act_dtype(sh.act)
     d, _ = dims_pair(sh, out=out)
     st = dev(inp["state"], torch.float32)
