@@ -340,3 +340,51 @@ def test_prefill_two_slice_workgroups_equal_single_row_calls(DK, DV, lengths, ou
         else:   # the oracle's value rounded to bf16, within one more bf16 unit
             assert out_err(o_g[:, b:b + 1, :n].astype(np.float64),
                            W.bf16_round(o_r.astype(np.float32))) <= 2 ** -7, b
+
+
+@pytest.mark.parametrize("rows", [1, 4])
+def test_prefill_graph_replay_matches_eager(rows):
+    """Two chained 128-token prefill calls (state carried) captured in one HIP
+    graph, at B = 1 (one column slice per scan workgroup) and B = 4 (two):
+    every replay, with eager work in between, equals the eager calls bit for
+    bit."""
+    torch = torch_mod()
+    sh = W.Shape("pfg", L=1, B=rows, T=256, HV=32, HK=16, DK=128, DV=128, S=1)
+    inp = W.prefill_inputs(sh, seed=3800 + rows)
+    st0 = W.random_state(sh, seed=3801 + rows)
+    A = act_dtype(sh.act)
+    d, _ = dims_pair(sh, T=128)
+    halves = [{k: dev(np.ascontiguousarray(inp[k][:, :, h * 128:(h + 1) * 128]), A)
+               for k in ("y", "g", "beta")} for h in range(2)]
+    ws = torch.empty(B().gdn_workspace_size(d), dtype=torch.uint8, device="cuda")
+
+    def run(st, outs):
+        for h in range(2):
+            B().gdn_prefill_chunked(d, halves[h]["y"], halves[h]["g"], halves[h]["beta"], st, None,
+                                    outs[h], 64, ws)
+
+    def fresh():
+        return dev(st0, torch.float32), [torch.empty((1, sh.B, 128, sh.HV, sh.DV), device="cuda")
+                                         for _ in range(2)]
+
+    st_e, o_e = fresh()
+    run(st_e, o_e)
+    torch.cuda.synchronize()
+    st_g, o_g = fresh()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        run(st_g, o_g)
+    torch.cuda.synchronize()
+    junk = torch.randn(512, 512, device="cuda")
+    for it in range(3):
+        st_g.copy_(dev(st0, torch.float32))
+        for o in o_g:
+            o.fill_(float("nan"))
+        graph.replay()
+        junk = junk @ junk.T / 512.0          # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(st_g, st_e), it
+        for h in range(2):
+            assert torch.equal(o_g[h], o_e[h]), (it, h)
