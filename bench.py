@@ -3,17 +3,23 @@
 
 Headline: the B8/T2 verification cohort (32 value heads, 16 qk heads,
 d_k = d_v = 128, bf16 inputs, fp32 state, rows 1 and 6 inactive, keep ~
-U{0,1,2} drawn per cycle).  One step is one decode cycle of a 30-layer
-hybrid stack: gdn_verify over the 30 GDN layers' state pools (one grouped
-launch) followed by gdn_commit of every layer (one grouped launch).  The 30
-pools (1.44 GiB of fp32 state) exceed the 256 MiB Infinity Cache, so state
-traffic is HBM traffic.  Metric: rows*heads/s = 30 * 8 * 32 per step / time.
+U{0,1,2} drawn per cycle) in a 30-layer hybrid stack, issued the way a model
+forward issues it: one gdn_verify per GDN layer (layer l+1's inputs exist
+only once layer l has run), then, once acceptance has fixed keep, one
+gdn_commit over all 30 layers.  The 30 layer pools (1.44 GiB of fp32 state)
+exceed the 256 MiB Infinity Cache, so state traffic is HBM traffic.
+Metric: rows*heads/s = 30 layers * 8 rows * 32 heads per cycle / time; the
+8 rows include the 2 inactive ones (active_rows_heads_per_s counts only 6).
 
-Also printed (in the same JSON line, under "extra"): the same cycle with one
-verify launch per layer captured in a HIP graph, the solo B1/T3 30-layer
-cycle, the B8/T4 rewind, the 1,024-token conv step and the chunked prefill.
+Every other measurement goes under "extra", each with its own roofline and,
+where the oracle can run it, a CPU baseline: the same cycle with one grouped
+verify launch over the 30 layers, the fused commit + verify (per layer and
+grouped), the solo B1/T3 30-layer cycle, the B8/T4 rewind, the 1,024-token
+conv step, the chunked prefill (B1, 4,096 tokens in 1,024-token calls), the
+ragged B8 prefill, the gated RMSNorm and its fused forms, and the measured
+ceilings (hand-written HBM stream kernels and a bf16 MFMA loop).
 
-  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--only NAME]
 """
 from __future__ import annotations
 
@@ -30,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
 L_POOL = 30
 
 
@@ -41,8 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only", default=None,
-                    help="run one secondary measurement (per_layer_graph, solo, rewind, conv_step, "
-                         "prefill) and print its JSON instead of the headline line")
+                    help="run one measurement (a key of SECTIONS) and print its JSON instead of "
+                         "the headline line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (used to "
                          "calibrate the FETCH_SIZE / WRITE_SIZE counters)")
@@ -63,8 +70,8 @@ def copy_probe(torch):
 
 def counted_traffic(key):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
-    (calibrated on a plain copy) for the kernel source they were taken on;
-    None when that source has changed since."""
+    (calibrated on a plain copy) for the kernel sources they were taken on;
+    None when that record is missing or a source has changed since."""
     import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
@@ -85,7 +92,7 @@ def log(msg):
 
 class Timer:
     """HIP events on torch's current stream, which is the stream every
-    libgdn call below is launched on."""
+    libgdn call below is launched on (graphs are replayed on it too)."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -96,8 +103,46 @@ class Timer:
         return e
 
 
+def graph_of(torch, fn):
+    """Captures fn() once in a HIP graph (on a side stream, after one eager
+    warm-up call) and returns it."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    return graph
+
+
+def time_graph(torch, graph, reps, warm=2):
+    """Average ms per replay of a captured graph, replays back to back
+    between two HIP events."""
+    for _ in range(warm):
+        graph.replay()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    a = tm.ev()
+    for _ in range(reps):
+        graph.replay()
+    b = tm.ev()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def roofline(bound, achieved, peak, unit, traffic_key, measured_peak=None, **kw):
+    r = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+         "frac": achieved / peak, "traffic": counted_traffic(traffic_key) if traffic_key else None}
+    if measured_peak:
+        r["measured_peak"] = measured_peak
+        r["frac_of_measured"] = achieved / measured_peak
+    r.update(kw)
+    return r
+
+
 def cohort_pools(torch, W, sh, L, seed):
-    """L layers of the cohort: every tensor on the GPU, stacked along the layer axis."""
+    """L layers of a verify workload: every tensor on the GPU, stacked along the layer axis."""
     big = sh.with_(L=L)
     rng = np.random.default_rng(seed)
     bf = torch.bfloat16 if sh.act == "bf16" else torch.float32
@@ -129,11 +174,11 @@ def cohort_pools(torch, W, sh, L, seed):
 
 
 def verify_bytes(sh, n_active_rows, L):
-    """Algorithmic bytes of one grouped verify launch: per active (layer, row):
-    the fp32 state read once (HV*DK*DV*4) and written T times as candidates,
-    the window inputs x (T*C) and conv cache (3*C) in the act dtype, g and
-    beta (2*T*HV), and the fp32 outputs (T*HV*DV*4); per layer the conv
-    weights (C*4)."""
+    """Algorithmic bytes of one verify launch over L layers: per active
+    (layer, row): the fp32 state read once (HV*DK*DV*4) and written T times as
+    candidates, the window inputs x (T*C) and conv cache (3*C) in the act
+    dtype, g and beta (2*T*HV), and the fp32 outputs (T*HV*DV*4); per layer
+    the conv weights (C*4)."""
     esz = 2 if sh.act == "bf16" else 4
     tile = sh.HV * sh.DK * sh.DV * 4
     per_row = tile * (1 + sh.T) + (sh.T + 3) * sh.C * esz + 2 * sh.T * sh.HV * esz \
@@ -164,59 +209,266 @@ def algorithmic_min_bytes(sh, keep, active, L):
     return L * (n_act * per_act + n_com * per_com + sh.C * 4 * esz)
 
 
-def stream_copy_gbs(torch):
-    """Device-to-device copy rate of a 1 GiB buffer (read + write bytes per
-    second), the practical ceiling of a kernel that streams memory."""
-    n = 1 << 28
-    a = torch.empty(n, device="cuda")
-    a.fill_(1.0)
-    b = torch.empty_like(a)
-    for _ in range(2):
-        b.copy_(a)
-    tm = Timer(torch)
-    e0 = tm.ev()
-    reps = 5
-    for _ in range(reps):
-        b.copy_(a)
-    e1 = tm.ev()
-    torch.cuda.synchronize()
-    gbs = 2 * n * 4 * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
-    del a, b
+def lazy_bytes(sh, keep_prev, act_rows, L):
+    """Algorithmic bytes of one fused commit + verify cycle over L layers:
+    per (layer, row) that replays or verifies, one state read, both windows'
+    x (2T rows) and the conv cache (3 rows), both windows' g and beta; per
+    committing row one state write and the conv-cache shift (3 rows read, 3
+    written); per active row the outputs; per layer the conv weights."""
+    esz = 2 if sh.act == "bf16" else 4
+    tile = sh.HV * sh.DK * sh.DV * 4
+    per = 0
+    for b in range(sh.B):
+        if act_rows[b] or keep_prev[b] > 0:
+            per += tile + (2 * sh.T + 3) * sh.C * esz + 4 * sh.T * sh.HV * esz
+        if keep_prev[b] > 0:
+            per += tile + 6 * sh.C * esz
+        if act_rows[b]:
+            per += sh.T * sh.HV * sh.DV * 4
+    return L * (per + sh.C * 4 * esz)
+
+
+# ---------------------------------------------------------------------------
+# Measured ceilings: hand-written stream kernels and a bf16 MFMA loop.
+
+def ceilings(torch, gb, W, args):
+    """Sustained HBM rates of hand-written stream kernels for the read:write
+    mixes of the path's kernels (read-only, write-only, copy 1:1, 1:2 as
+    verify at T=2, 1:3 as verify at T=3, 2:1), each over buffers of 512 MiB
+    to 1 GiB, best over a small sweep of grid size, vectors per thread and
+    non-temporal vs plain access; and the dense bf16 MFMA rate of a loop of
+    independent v_mfma_f32_16x16x32_bf16 chains."""
+    from gated_deltanet_recurrence_conv_amd import ceiling as ce
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    mixes = {"read": (1, 0), "write": (0, 1), "copy": (1, 1), "r1w2": (1, 2), "r1w3": (1, 3),
+             "r2w1": (2, 1)}
+    total_bytes = 1 << 30
+    res = {"cus": cus}
+    for name, (nr, nw) in mixes.items():
+        nbuf = nr + nw
+        per = (total_bytes // max(1, nbuf)) // 16 * 16 if nbuf > 1 else total_bytes
+        n_vec = per // 16
+        bufs = [torch.empty(per // 4, dtype=torch.float32, device="cuda") for _ in range(nbuf)]
+        for bb in bufs:
+            bb.fill_(1.0)
+        sink = torch.empty(cus * 64 * 4, dtype=torch.float32, device="cuda")
+        srcs, dsts = bufs[:nr], bufs[nr:]
+        best = (0.0, None)
+        for mult in (4, 8, 16):
+            for unroll in (2, 4, 8):
+                for nt in (True, False):
+                    grid = cus * mult
+                    if not dsts and grid * 4 > sink.numel():
+                        continue
+
+                    def run():
+                        ce.gdn_ceiling_stream(srcs, dsts, n_vec, sink=sink, grid=grid,
+                                              unroll=unroll, nontemporal=nt)
+                    run()
+                    torch.cuda.synchronize()
+                    tm = Timer(torch)
+                    reps = 4
+                    a = tm.ev()
+                    for _ in range(reps):
+                        run()
+                    b = tm.ev()
+                    torch.cuda.synchronize()
+                    ms = a.elapsed_time(b) / reps
+                    gbs = n_vec * 16 * nbuf / (ms / 1e3) / 1e9
+                    if gbs > best[0]:
+                        best = (gbs, dict(grid_per_cu=mult, unroll=unroll, nontemporal=nt))
+        res[name + "_gbs"] = best[0]
+        res[name + "_config"] = best[1]
+        del bufs, sink
+        torch.cuda.empty_cache()
+    out = torch.empty(cus * 4 * 256 * 32, dtype=torch.float32, device="cuda")
+    best = 0.0
+    for mult in (1, 2, 4):
+        grid, iters = cus * mult, 4000
+        ce.gdn_ceiling_mfma_bf16(out, grid, iters)
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        a = tm.ev()
+        ce.gdn_ceiling_mfma_bf16(out, grid, iters)
+        b = tm.ev()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = max(best, grid * 4 * iters * 8 * 16384 / (ms / 1e3) / 1e12)
+    res["mfma_bf16_tflops"] = best
+    del out
     torch.cuda.empty_cache()
-    return gbs
+    return res
 
 
-def headline(torch, gb, W, args):
-    """The headline cycle: one grouped verify over the 30 layer pools, then one
-    grouped commit with a fresh device keep vector.  The K timed cycles are
-    captured once in a HIP graph (as a decode loop issues them) and replayed,
-    so the time is the GPU's, not the host's launch rate.  The verify
-    kernel's average launch time for the roofline comes from a separate run
-    of back-to-back verify launches (verify writes only candidate slots, so
-    repeating it changes nothing)."""
+# ---------------------------------------------------------------------------
+# The oracle beside the GPU: single-threaded and fanned out over host cores.
+
+def oracle_rate(make_stream, units_per_call, unit, sample, budget_s):
+    """Runs an oracle call stream for about budget_s on one thread, then one
+    independent stream per host thread (up to 16; the C oracle runs outside
+    the GIL) for 3/4 of that.  make_stream(seed) returns a function doing one
+    call (or one fixed group of calls) of units_per_call units."""
+    import concurrent.futures as cf
+    step = make_stream(0)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        step()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    workers = max(1, min(os.cpu_count() or 1, 16))
+    par_budget = budget_s * 0.75
+
+    def stream(seed):
+        f = make_stream(seed)
+        k = 0
+        t_end = time.perf_counter() + par_budget
+        while time.perf_counter() < t_end:
+            f()
+            k += 1
+        return k
+
+    t1 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        counts = list(ex.map(stream, range(100, 100 + workers)))
+    el2 = time.perf_counter() - t1
+    return dict(value=n * units_per_call / el, unit=unit, cores=1, kind="oracle",
+                sample="%d calls of %s in %.1f s, single-threaded float64 C oracle incl. "
+                       "marshalling; host: %s, %d cpus" % (n, sample, el,
+                                                           platform.processor() or platform.machine(),
+                                                           os.cpu_count() or 0),
+                all_cores=dict(value=sum(counts) * units_per_call / el2, cores=workers,
+                               sample="%d calls over %d threads in %.1f s, one independent stream "
+                                      "per thread" % (sum(counts), workers, el2)))
+
+
+def cpu_cohort(W, budget_s):
+    """verify + commit layer-cycles of the B8/T2 cohort (8 rows x 32 heads, 6 active)."""
+    import oracle
+    sh = W.COHORT
+    inp = W.verify_inputs(sh, seed=4242)
+    od = oracle.Dims(L=1, B=sh.B, T=sh.T, HV=sh.HV, HK=sh.HK, DK=sh.DK, DV=sh.DV, S=sh.S)
+
+    def make(seed):
+        r = np.random.default_rng(seed)
+        s = dict(st=inp["state"].copy(), cs=inp["conv_state"].copy(), cur=inp["cur"].copy())
+
+        def step():
+            keep = W.keep_uniform(r, sh, inp["active"])
+            s["st"], _, _ = oracle.verify(od, inp["x"], inp["conv_w"], None, s["cs"], inp["g"],
+                                          inp["beta"], s["st"], s["cur"], inp["active"])
+            s["cs"], s["cur"], _ = oracle.commit(od, inp["x"], s["cs"], s["cur"], keep, inp["active"])
+        return step
+    return oracle_rate(make, sh.B * sh.HV, "rows*heads/s",
+                       "one verify+commit layer-cycle of the B8/T2 cohort (8 rows x 32 heads, 6 "
+                       "active)", budget_s)
+
+
+def cpu_solo(W, budget_s):
+    """verify + commit layer-cycles of the solo B1/T3 shape (one of its 30
+    independent layers per call), keep by prefix acceptance p = 0.8."""
+    import oracle
+    sh = W.SOLO.with_(L=1)
+    inp = W.verify_inputs(sh, seed=4343)
+    od = oracle.Dims(L=1, B=1, T=sh.T, HV=sh.HV, HK=sh.HK, DK=sh.DK, DV=sh.DV, S=sh.S)
+
+    def make(seed):
+        r = np.random.default_rng(seed)
+        s = dict(st=inp["state"].copy(), cs=inp["conv_state"].copy(), cur=inp["cur"].copy())
+
+        def step():
+            keep = W.keep_prefix_acceptance(r, sh)
+            s["st"], _, _ = oracle.verify(od, inp["x"], inp["conv_w"], None, s["cs"], inp["g"],
+                                          inp["beta"], s["st"], s["cur"], None)
+            s["cs"], s["cur"], _ = oracle.commit(od, inp["x"], s["cs"], s["cur"], keep, None)
+        return step
+    return oracle_rate(make, sh.HV, "rows*heads/s",
+                       "one verify+commit layer-cycle of the solo B1/T3 shape (1 row x 32 heads)",
+                       budget_s)
+
+
+def cpu_rewind(W, budget_s):
+    """Rewind calls of the B8/T4 shape (one layer per call), keep ~ U{0..4}."""
+    import oracle
+    sh = W.REWIND
+    inp = W.verify_inputs(sh, seed=4444)
+    od = oracle.Dims(L=1, B=sh.B, T=sh.T, HV=sh.HV, HK=sh.HK, DK=sh.DK, DV=sh.DV, S=sh.S)
+
+    def make(seed):
+        r = np.random.default_rng(seed)
+
+        def step():
+            keep = W.keep_uniform(r, sh)
+            oracle.rewind(od, inp["x"], inp["conv_w"], None, inp["conv_state"], inp["g"],
+                          inp["beta"], inp["state"], inp["cur"], keep)
+        return step
+    return oracle_rate(make, sh.B * sh.HV, "rows*heads/s",
+                       "one B8/T4 rewind layer-call (8 rows x 32 heads, keep ~ U{0..4})", budget_s)
+
+
+def cpu_prefill(W, budget_s):
+    """Token-sequential prefill of the Qwen head shape (32 value / 16 qk heads,
+    d = 128), 64 tokens per call with the state carried."""
+    import oracle
+    sh = W.PREFILL
+    n = 64
+    inp = W.prefill_inputs(sh, seed=4545, tokens=n)
+    od = oracle.Dims(L=1, B=1, T=n, HV=sh.HV, HK=sh.HK, DK=sh.DK, DV=sh.DV, S=1)
+
+    def make(seed):
+        s = dict(st=inp["state"].copy())
+
+        def step():
+            s["st"], _, _ = oracle.prefill(od, inp["y"], inp["g"], inp["beta"], s["st"], inp["cur"])
+        return step
+    return oracle_rate(make, n, "tokens/s",
+                       "a 64-token prefill call at 32 value / 16 qk heads, d = 128, state carried",
+                       budget_s)
+
+
+# ---------------------------------------------------------------------------
+# GPU legs.
+
+def per_layer_cycle(torch, gb, W, args, ceil):
+    """The headline cycle, as a model forward issues it: gdn_verify on each of
+    the 30 layers in turn (one launch per layer), then one gdn_commit over all
+    30 layers with the cycle's keep (acceptance needs the last layer's
+    logits, so no layer commits before every layer has verified).  The K
+    timed cycles (fresh keep each) are captured once in a HIP graph and
+    replayed, so the time is the GPU's, not the host's launch rate.  The
+    per-launch verify time for the roofline comes from a graph of 30
+    per-layer verify launches replayed back to back (verify writes only
+    candidate slots, so repeating it changes nothing)."""
     sh = W.COHORT
     big, t, rng, act_rows = cohort_pools(torch, W, sh, L_POOL, 1001)
-    d = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
-                     out="f32")
+    d1 = gb.make_dims(1, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16", out="f32")
+    dL = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
+                      out="f32")
     n = args.steps + args.warmup
     keeps = np.stack([W.keep_uniform(rng, sh, act_rows) for _ in range(n)]).astype(np.int32)
     keep_d = torch.from_numpy(keeps).cuda()
 
-    def step(i):
-        gb.gdn_verify(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
-                      t["state"], t["cur"], t["o"], t["active"], t["err"])
-        gb.gdn_commit(d, t["x"], t["conv_state"], t["cur"], keep_d[i], t["active"], t["err"])
+    def verify_layers():
+        for l in range(L_POOL):
+            sl = slice(l, l + 1)
+            gb.gdn_verify(d1, t["x"][sl], t["conv_w"][sl], None, t["conv_state"][sl],
+                          t["g"][sl], t["beta"][sl], t["state"][sl], t["cur"][sl], t["o"][sl],
+                          t["active"], t["err"])
+
+    def cycle(i):
+        verify_layers()
+        gb.gdn_commit(dL, t["x"], t["conv_state"], t["cur"], keep_d[i], t["active"], t["err"])
 
     for i in range(args.warmup):
-        step(i)
+        cycle(i)
     torch.cuda.synchronize()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=s):
+
+    def timed():
         for i in range(args.warmup, n):
-            step(i)
-    torch.cuda.synchronize()
+            cycle(i)
+    graph = graph_of(torch, timed)
     tm = Timer(torch)
     start = tm.ev()
     graph.replay()
@@ -224,41 +476,37 @@ def headline(torch, gb, W, args):
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     assert int(t["err"].item()) == 0, "device error word set"
-    # verify alone, back to back
-    reps = 20
-    v0 = tm.ev()
-    for _ in range(reps):
-        gb.gdn_verify(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
-                      t["state"], t["cur"], t["o"], t["active"], t["err"])
-    v1 = tm.ev()
-    torch.cuda.synchronize()
-    verify_ms = v0.elapsed_time(v1) / reps
+    del graph
+    vgraph = graph_of(torch, verify_layers)
+    verify_ms = time_graph(torch, vgraph, 10) / L_POOL
     assert int(t["err"].item()) == 0, "device error word set"
     n_act = int(act_rows.sum())
-    vb = verify_bytes(sh, n_act, L_POOL)
+    vb = verify_bytes(sh, n_act, 1)
     cb = float(np.mean([commit_bytes(sh, keeps[i], act_rows, L_POOL) for i in range(args.warmup, n)]))
     amin = float(np.mean([algorithmic_min_bytes(sh, keeps[i], act_rows, L_POOL)
                           for i in range(args.warmup, n)]))
     ms_step = total_ms / args.steps
-    rows_heads = L_POOL * sh.B * sh.HV
-    res = dict(ms_per_step=ms_step, value=rows_heads * args.steps / (total_ms / 1e3),
-               verify_ms=verify_ms, verify_bytes=vb, commit_bytes=cb,
-               verify_gbs=vb / (verify_ms / 1e3) / 1e9,
-               cycle_gbs=(vb + cb) / (ms_step / 1e3) / 1e9,
+    res = dict(ms_per_step=ms_step, value=L_POOL * sh.B * sh.HV / (ms_step / 1e3),
+               active_rows_heads_per_s=L_POOL * n_act * sh.HV / (ms_step / 1e3),
+               launches_per_step=L_POOL + 1, verify_ms_per_layer=verify_ms,
+               verify_bytes_per_layer=vb, commit_bytes=cb,
+               cycle_gbs=(L_POOL * vb + cb) / (ms_step / 1e3) / 1e9,
                algorithmic_min_bytes_per_cycle=amin,
-               algorithmic_min_gbs=amin / (ms_step / 1e3) / 1e9,
-               active_rows_heads_per_s=L_POOL * n_act * sh.HV * args.steps / (total_ms / 1e3))
-    del t, graph
+               algorithmic_min_gbs=amin / (ms_step / 1e3) / 1e9)
+    res["roofline"] = roofline("hbm", vb / (verify_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                               "recurrent_kernel_verify_b8_t2_l1",
+                               measured_peak=ceil.get("r1w2_gbs"),
+                               kernel="gdn::recurrent_kernel<128,128,bf16> (verify, one layer)",
+                               algorithmic_bytes_per_launch=vb, avg_launch_ms=verify_ms)
+    del t, vgraph
     torch.cuda.empty_cache()
     return res
 
 
-def lazy_cycle(torch, gb, W, args):
-    """The cohort cycle with the commit folded into the next verify
-    (gdn_verify_lazy): each cycle replays the previous cycle's accepted
-    tokens from the snapshot, writes the committed state once in place, and
-    verifies the new window without candidate writes.  Same pools, keep
-    sequence and graph replay as the headline."""
+def grouped_cycle(torch, gb, W, args, ceil):
+    """The cycle with one grouped verify launch over the 30 layer pools and one
+    grouped commit (a launch shape for independent layers; a model forward
+    issues per-layer verifies), graph-replayed as the headline."""
     sh = W.COHORT
     big, t, rng, act_rows = cohort_pools(torch, W, sh, L_POOL, 1001)
     d = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
@@ -267,103 +515,123 @@ def lazy_cycle(torch, gb, W, args):
     keeps = np.stack([W.keep_uniform(rng, sh, act_rows) for _ in range(n)]).astype(np.int32)
     keep_d = torch.from_numpy(keeps).cuda()
 
-    def cycle(i):
-        # the previous window's inputs are the same pool tensors (the bench
-        # does not change x between cycles); keep_prev is the previous keep
-        gb.gdn_verify_lazy(d, t["x"] if i else None, t["g"] if i else None,
-                           t["beta"] if i else None, keep_d[i - 1] if i else None, t["x"],
-                           t["conv_w"], None, t["conv_state"], t["g"], t["beta"], t["state"],
-                           t["cur"], t["o"], t["active"], t["err"])
+    def verify():
+        gb.gdn_verify(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
+                      t["state"], t["cur"], t["o"], t["active"], t["err"])
+
+    def step(i):
+        verify()
+        gb.gdn_commit(d, t["x"], t["conv_state"], t["cur"], keep_d[i], t["active"], t["err"])
 
     for i in range(args.warmup):
-        cycle(i)
+        step(i)
     torch.cuda.synchronize()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=s):
+
+    def timed():
         for i in range(args.warmup, n):
-            cycle(i)
-    torch.cuda.synchronize()
+            step(i)
+    graph = graph_of(torch, timed)
     tm = Timer(torch)
     start = tm.ev()
     graph.replay()
     end = tm.ev()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    total_ms = start.elapsed_time(end)
     assert int(t["err"].item()) == 0, "device error word set"
-    esz, tile = 2, sh.HV * sh.DK * sh.DV * 4
-    byts = []
-    for i in range(args.warmup, n):
-        kp = keeps[i - 1]
-        per = 0
-        for b in range(sh.B):
-            if act_rows[b] or kp[b] > 0:
-                per += tile + (2 * sh.T + 3) * sh.C * esz + 4 * sh.T * sh.HV * esz
-            if kp[b] > 0:
-                per += tile + 6 * sh.C * esz
-            if act_rows[b]:
-                per += sh.T * sh.HV * sh.DV * 4
-        byts.append(L_POOL * (per + sh.C * 4 * esz))
-    per_cycle = float(np.mean(byts))
+    reps = 20
+    v0 = tm.ev()
+    for _ in range(reps):
+        verify()
+    v1 = tm.ev()
+    torch.cuda.synchronize()
+    verify_ms = v0.elapsed_time(v1) / reps
+    n_act = int(act_rows.sum())
+    vb = verify_bytes(sh, n_act, L_POOL)
+    cb = float(np.mean([commit_bytes(sh, keeps[i], act_rows, L_POOL) for i in range(args.warmup, n)]))
+    amin = float(np.mean([algorithmic_min_bytes(sh, keeps[i], act_rows, L_POOL)
+                          for i in range(args.warmup, n)]))
+    ms_step = total_ms / args.steps
+    res = dict(ms_per_step=ms_step, rows_heads_per_s=L_POOL * sh.B * sh.HV / (ms_step / 1e3),
+               active_rows_heads_per_s=L_POOL * n_act * sh.HV / (ms_step / 1e3),
+               launches_per_step=2, verify_ms=verify_ms, verify_bytes=vb, commit_bytes=cb,
+               cycle_gbs=(vb + cb) / (ms_step / 1e3) / 1e9,
+               algorithmic_min_bytes_per_cycle=amin,
+               algorithmic_min_gbs=amin / (ms_step / 1e3) / 1e9)
+    res["roofline"] = roofline("hbm", vb / (verify_ms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                               "recurrent_kernel_verify_b8_t2_l30",
+                               measured_peak=ceil.get("r1w2_gbs"),
+                               kernel="gdn::recurrent_kernel<128,128,bf16> (verify, 30 layers)",
+                               algorithmic_bytes_per_launch=vb, avg_launch_ms=verify_ms)
     del t, graph
-    torch.cuda.empty_cache()
-    return dict(ms_per_cycle=ms, rows_heads_per_s=L_POOL * sh.B * sh.HV / (ms / 1e3),
-                bytes_per_cycle=per_cycle, gbs=per_cycle / (ms / 1e3) / 1e9,
-                launches_per_cycle=2)
-
-
-def per_layer_graph(torch, gb, W, args):
-    """The same cycle with one verify launch per layer (as a model forward
-    issues them), captured once in a HIP graph and replayed."""
-    sh = W.COHORT
-    big, t, rng, act_rows = cohort_pools(torch, W, sh, L_POOL, 1002)
-    d1 = gb.make_dims(1, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16", out="f32")
-    dL = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
-                      out="f32")
-    keep_cur = torch.zeros(sh.B, dtype=torch.int32, device="cuda")
-    n = args.steps + args.warmup
-    keeps = torch.from_numpy(np.stack([W.keep_uniform(rng, sh, act_rows) for _ in range(n)])
-                             .astype(np.int32)).cuda()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-
-    def cycle():
-        for l in range(L_POOL):
-            sl = slice(l, l + 1)
-            gb.gdn_verify(d1, t["x"][sl], t["conv_w"][sl], None, t["conv_state"][sl],
-                          t["g"][sl], t["beta"][sl], t["state"][sl], t["cur"][sl], t["o"][sl],
-                          t["active"], t["err"])
-        gb.gdn_commit(dL, t["x"], t["conv_state"], t["cur"], keep_cur, t["active"], t["err"])
-
-    with torch.cuda.stream(s):
-        cycle()                       # warm-up outside the capture
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=s):
-        cycle()
-    torch.cuda.synchronize()
-    for i in range(args.warmup):
-        keep_cur.copy_(keeps[i])
-        graph.replay()
-    torch.cuda.synchronize()
-    tm = Timer(torch)
-    start = tm.ev()
-    for i in range(args.warmup, n):
-        keep_cur.copy_(keeps[i])
-        graph.replay()
-    end = tm.ev()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    assert int(t["err"].item()) == 0
-    res = dict(ms_per_step=ms, rows_heads_per_s=L_POOL * sh.B * sh.HV / (ms / 1e3),
-               launches_per_step=L_POOL + 1)
-    del graph, t
     torch.cuda.empty_cache()
     return res
 
 
-def solo(torch, gb, W, args):
+def lazy_legs(torch, gb, W, args, ceil):
+    """The cohort cycle with the commit folded into the next verify
+    (gdn_verify_lazy): each cycle replays the previous cycle's accepted
+    tokens from the snapshot, writes the committed state once in place, and
+    verifies the new window without candidate writes.  Per layer (30 calls
+    per cycle, as a model forward issues them) and grouped (one call over the
+    30 layers); same pools, keep sequence and graph replay as the headline.
+    Each call is two launches (the replay-and-verify kernel and the
+    conv-cache shift); the roofline prices the whole cycle's bytes against
+    its time."""
+    sh = W.COHORT
+    big, t, rng, act_rows = cohort_pools(torch, W, sh, L_POOL, 1001)
+    d1 = gb.make_dims(1, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16", out="f32")
+    dL = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
+                      out="f32")
+    n = args.steps + args.warmup
+    keeps = np.stack([W.keep_uniform(rng, sh, act_rows) for _ in range(n)]).astype(np.int32)
+    keep_d = torch.from_numpy(keeps).cuda()
+
+    def call(d, sl, i):
+        # the previous window's inputs are the same pool tensors (the bench
+        # does not change x between cycles); keep_prev is the previous keep
+        gb.gdn_verify_lazy(d, t["x"][sl] if i else None, t["g"][sl] if i else None,
+                           t["beta"][sl] if i else None, keep_d[i - 1] if i else None, t["x"][sl],
+                           t["conv_w"][sl], None, t["conv_state"][sl], t["g"][sl], t["beta"][sl],
+                           t["state"][sl], t["cur"][sl], t["o"][sl], t["active"], t["err"])
+
+    def cycle_layers(i):
+        for l in range(L_POOL):
+            call(d1, slice(l, l + 1), i)
+
+    def cycle_grouped(i):
+        call(dL, slice(0, L_POOL), i)
+
+    res = {}
+    byts = float(np.mean([lazy_bytes(sh, keeps[i - 1], act_rows, L_POOL) for i in range(args.warmup, n)]))
+    for name, cyc, launches in (("per_layer", cycle_layers, 2 * L_POOL), ("grouped", cycle_grouped, 2)):
+        for i in range(args.warmup):
+            cyc(i)
+        torch.cuda.synchronize()
+
+        def timed():
+            for i in range(args.warmup, n):
+                cyc(i)
+        graph = graph_of(torch, timed)
+        tm = Timer(torch)
+        start = tm.ev()
+        graph.replay()
+        end = tm.ev()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / args.steps
+        assert int(t["err"].item()) == 0, "device error word set"
+        del graph
+        gbs = byts / (ms / 1e3) / 1e9
+        res[name] = dict(ms_per_cycle=ms, rows_heads_per_s=L_POOL * sh.B * sh.HV / (ms / 1e3),
+                         bytes_per_cycle=byts, gbs=gbs, launches_per_cycle=launches,
+                         roofline=roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", None,
+                                           measured_peak=ceil.get("copy_gbs"),
+                                           kernel="recurrent_kernel (lazy) + window_kernel, whole cycle"))
+    del t
+    torch.cuda.empty_cache()
+    return res
+
+
+def solo(torch, gb, W, args, ceil):
     """B=1, T=3 (two drafts + bonus), 30 independent layers in one grouped
     launch, keep by prefix acceptance p=0.8, state carried across cycles."""
     sh = W.SOLO
@@ -373,38 +641,48 @@ def solo(torch, gb, W, args):
     keeps = torch.from_numpy(np.stack([W.keep_prefix_acceptance(rng, sh) for _ in range(cycles)])
                              .astype(np.int32)).cuda()
 
-    def cyc(i):
+    def verify():
         gb.gdn_verify(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
                       t["state"], t["cur"], t["o"], None, t["err"])
+
+    def cyc(i):
+        verify()
         gb.gdn_commit(d, t["x"], t["conv_state"], t["cur"], keeps[i], None, t["err"])
 
     for i in range(10):
         cyc(i)
     torch.cuda.synchronize()
+
+    def timed():
+        for i in range(cycles):
+            cyc(i)
+    graph = graph_of(torch, timed)
     tm = Timer(torch)
-    marks = []
     start = tm.ev()
-    for i in range(cycles):
-        v0 = tm.ev()
-        gb.gdn_verify(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
-                      t["state"], t["cur"], t["o"], None, t["err"])
-        v1 = tm.ev()
-        gb.gdn_commit(d, t["x"], t["conv_state"], t["cur"], keeps[i], None, t["err"])
-        marks.append((v0, v1))
+    graph.replay()
     end = tm.ev()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / cycles
-    vms = float(np.mean([a.elapsed_time(b) for a, b in marks]))
+    del graph
+    vgraph = graph_of(torch, lambda: [verify() for _ in range(20)])
+    vms = time_graph(torch, vgraph, 5) / 20
     vb = verify_bytes(sh, 1, sh.L)
     assert int(t["err"].item()) == 0
-    del t
+    del t, vgraph
     torch.cuda.empty_cache()
     return dict(ms_per_cycle=ms, rows_heads_per_s=sh.L * sh.HV / (ms / 1e3), verify_ms=vms,
-                verify_gbs=vb / (vms / 1e3) / 1e9)
+                verify_bytes=vb,
+                roofline=roofline("hbm", vb / (vms / 1e3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                                  "recurrent_kernel_verify_b1_t3_l30",
+                                  measured_peak=ceil.get("r1w3_gbs"),
+                                  kernel="gdn::recurrent_kernel<128,128,bf16> (verify, B1/T3, 30 layers)",
+                                  algorithmic_bytes_per_launch=vb, avg_launch_ms=vms))
 
 
-def rewind(torch, gb, W, args):
-    """B=8, T=4 captured window, keep ~ U{0..4}, 30 layer pools in one grouped call."""
+def rewind(torch, gb, W, args, ceil):
+    """B=8, T=4 captured window, keep ~ U{0..4}, 30 layer pools in one grouped
+    call (the replay kernel, then the conv-cache shift); 20 calls with fresh
+    keep vectors captured in one HIP graph."""
     sh = W.REWIND
     big, t, rng, act_rows = cohort_pools(torch, W, sh.with_(L=1), L_POOL, 3003)
     d = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
@@ -412,33 +690,35 @@ def rewind(torch, gb, W, args):
     reps = 20
     keeps_np = np.stack([W.keep_uniform(rng, sh) for _ in range(reps + 3)]).astype(np.int32)
     keeps = torch.from_numpy(keeps_np).cuda()
+
+    def call(i):
+        gb.gdn_rewind(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
+                      t["state"], t["cur"], keeps[i], None, t["err"])
+
     for i in range(3):
-        gb.gdn_rewind(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
-                      t["state"], t["cur"], keeps[i], None, t["err"])
+        call(i)
     torch.cuda.synchronize()
-    tm = Timer(torch)
-    start = tm.ev()
-    for i in range(3, reps + 3):
-        gb.gdn_rewind(d, t["x"], t["conv_w"], None, t["conv_state"], t["g"], t["beta"],
-                      t["state"], t["cur"], keeps[i], None, t["err"])
-    end = tm.ev()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / reps
+    graph = graph_of(torch, lambda: [call(i) for i in range(3, reps + 3)])
+    ms = time_graph(torch, graph, 1, warm=1) / reps
     tile = sh.HV * sh.DK * sh.DV * 4
     k = keeps_np[3:]
     # per committing (layer, row): state read + written, keep tokens of x/g/beta,
-    # conv cache read + written (3 rows each)
+    # conv cache read + written (3 rows each) and the conv weights' share
     per_call = np.mean([L_POOL * sum(2 * tile + kk * (sh.C * 2 + 4 * sh.HV) + 9 * sh.C * 2
                                      for kk in row if kk > 0) for row in k])
     assert int(t["err"].item()) == 0
-    del t
+    del t, graph
     torch.cuda.empty_cache()
-    return dict(ms_per_call=ms, bytes_per_call=float(per_call),
-                gbs=per_call / (ms / 1e3) / 1e9,
-                rows_heads_per_s=L_POOL * sh.B * sh.HV / (ms / 1e3))
+    gbs = per_call / (ms / 1e3) / 1e9
+    return dict(ms_per_call=ms, bytes_per_call=float(per_call), gbs=gbs,
+                rows_heads_per_s=L_POOL * sh.B * sh.HV / (ms / 1e3),
+                roofline=roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", "rewind_b8_t4_l30",
+                                  measured_peak=ceil.get("copy_gbs"),
+                                  kernel="gdn::recurrent_kernel (rewind) + gdn::window_kernel, per call",
+                                  algorithmic_bytes_per_launch=float(per_call), avg_launch_ms=ms))
 
 
-def conv_step(torch, gb, W, args):
+def conv_step(torch, gb, W, args, ceil):
     """The standalone conv over a 1,024-token prefill call, 10 buffers rotated.
     One call is ~10 us of GPU work, less than the host needs to issue it, so
     the 10 calls are captured once in a HIP graph and the graph is replayed."""
@@ -454,29 +734,24 @@ def conv_step(torch, gb, W, args):
     for i in range(nb):
         gb.gdn_conv_step(d, xs[i], w, None, cs, ys[i], None, True)
     torch.cuda.synchronize()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=s):
-        for i in range(nb):
-            gb.gdn_conv_step(d, xs[i], w, None, cs, ys[i], None, True)
-    torch.cuda.synchronize()
-    for _ in range(2):
-        graph.replay()
-    torch.cuda.synchronize()
-    replays = 10
-    tm = Timer(torch)
-    start = tm.ev()
-    for _ in range(replays):
-        graph.replay()
-    end = tm.ev()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / (replays * nb)
+    graph = graph_of(torch, lambda: [gb.gdn_conv_step(d, xs[i], w, None, cs, ys[i], None, True)
+                                     for i in range(nb)])
+    ms = time_graph(torch, graph, 10) / nb
     byts = 2 * sh.T * C * 2 + C * 4 * 2 + 6 * C * 2
-    return dict(tokens=sh.T, ms_per_call=ms, gbs=byts / (ms / 1e3) / 1e9)
+    gbs = byts / (ms / 1e3) / 1e9
+    return dict(tokens=sh.T, ms_per_call=ms, bytes_per_call=byts, gbs=gbs,
+                roofline=roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", "conv_kernel_t1024_c8192",
+                                  measured_peak=ceil.get("copy_gbs"), kernel="gdn::conv_kernel<bf16,8>",
+                                  algorithmic_bytes_per_launch=byts, avg_launch_ms=ms))
 
 
-def prefill(torch, gb, W, args):
+def prefill_flops(tokens, HV, d, chunk=64):
+    """Algorithmic flops of the chunked form per token-head (triangular-aware):
+    6 d^2 + 5 C d + C^2 / 3."""
+    return (6 * d * d + 5 * chunk * d + chunk * chunk / 3.0) * tokens * HV
+
+
+def prefill(torch, gb, W, args, ceil):
     """Chunked prefill of 4,096-token prompts in 1,024-token calls (chunk 64),
     32 value / 16 qk heads, d = 128, bf16 inputs and outputs, fp32 state;
     10 prompt buffers (640 MiB of y) rotated so inputs come from HBM."""
@@ -509,11 +784,18 @@ def prefill(torch, gb, W, args):
     for i in range(2):
         prompt(i)
     torch.cuda.synchronize()
+    # per-call time: the calls of 10 prompts captured in one graph (the state
+    # is not re-zeroed inside it, so only prefill launches are timed; it stays
+    # bounded, the gates decay it)
+    graph = graph_of(torch, lambda: [gb.gdn_prefill_chunked(d, ys[i][c], gs[i][c], bs[i][c], st,
+                                                            None, o, 64, ws)
+                                     for i in range(nb) for c in range(calls)])
+    prompt_ms = time_graph(torch, graph, 3) / nb
+    del graph
+    # per-call time by HIP events around each eager call
     tm = Timer(torch)
-    reps = 20
     marks = []
-    start = tm.ev()
-    for r in range(reps):
+    for r in range(8):
         i = r % nb
         st.zero_()
         for c in range(calls):
@@ -521,29 +803,36 @@ def prefill(torch, gb, W, args):
             gb.gdn_prefill_chunked(d, ys[i][c], gs[i][c], bs[i][c], st, None, o, 64, ws)
             e1 = tm.ev()
             marks.append((e0, e1))
-    end = tm.ev()
     torch.cuda.synchronize()
-    call_ms = float(np.mean([a.elapsed_time(b) for a, b in marks]))
-    total_ms = start.elapsed_time(end)
-    Cc, dd = 64, sh.DK
-    flop_tok_head = 6 * dd * dd + 5 * Cc * dd + Cc * Cc / 3.0
-    flops = flop_tok_head * sh.T * sh.HV
+    call_ms_events = float(np.mean([a.elapsed_time(b) for a, b in marks]))
+    call_ms = prompt_ms / calls
+    flops = prefill_flops(sh.T, sh.HV, sh.DK)
     byts = sh.T * C * 2 + 2 * sh.T * sh.HV * 2 + 2 * sh.HV * sh.DK * sh.DV * 4 \
         + sh.T * sh.HV * sh.DV * 2
     ai = flops / byts
-    attainable = min(2500.0, ai * HBM_PEAK_GBS / 1e3)   # TFLOP/s
+    attainable = min(BF16_MFMA_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)   # TFLOP/s
     tflops = flops / (call_ms / 1e3) / 1e12
+    gbs = byts / (call_ms / 1e3) / 1e9
+    meas = None
+    if ceil.get("mfma_bf16_tflops") and ceil.get("copy_gbs"):
+        meas = min(ceil["mfma_bf16_tflops"], ai * ceil["copy_gbs"] / 1e3)
     del ys, gs, bs
     torch.cuda.empty_cache()
-    return dict(call_ms=call_ms, tokens_per_s=calls * sh.T * reps / (total_ms / 1e3),
+    return dict(call_ms=call_ms, call_ms_eager_events=call_ms_events,
+                tokens_per_s=sh.T / (call_ms / 1e3),
                 flop_per_call=flops, bytes_per_call=byts, flop_per_byte=ai,
-                achieved_tflops=tflops, mfma_peak_tflops=2500.0,
-                frac_of_mfma_peak=tflops / 2500.0, attainable_tflops=attainable,
-                frac_of_attainable=tflops / attainable,
-                hbm_gbs=byts / (call_ms / 1e3) / 1e9, workspace_bytes=ws.numel())
+                achieved_tflops=tflops, frac_of_mfma_peak=tflops / BF16_MFMA_PEAK_TFLOPS,
+                attainable_tflops=attainable, frac_of_attainable=tflops / attainable,
+                hbm_gbs=gbs, workspace_bytes=ws.numel(),
+                roofline=roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", "prefill_b1_t1024",
+                                  kernel="prefill_prep_kernel + prefill_scan_kernel, per call",
+                                  algorithmic_bytes_per_launch=byts, avg_launch_ms=call_ms,
+                                  achieved_tflops=tflops, attainable_tflops=attainable,
+                                  measured_attainable_tflops=meas,
+                                  frac_of_measured_attainable=(tflops / meas) if meas else None))
 
 
-def prefill_ragged(torch, gb, W, args):
+def prefill_ragged(torch, gb, W, args, ceil):
     """Eight prompts of unequal length (seeded, 64..1,024 tokens) prefilled in
     one 1,024-token launch into their own rows of a B8 state (32 value / 16
     qk heads, d = 128, bf16 in and out); tokens/s counts real prompt tokens."""
@@ -570,24 +859,22 @@ def prefill_ragged(torch, gb, W, args):
     for _ in range(3):
         gb.gdn_prefill_ragged(d, y, g, b, st, None, o, lens, 64, ws)
     torch.cuda.synchronize()
-    reps = 20
-    tm = Timer(torch)
-    start = tm.ev()
-    for _ in range(reps):
-        gb.gdn_prefill_ragged(d, y, g, b, st, None, o, lens, 64, ws)
-    end = tm.ev()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / reps
+    graph = graph_of(torch, lambda: [gb.gdn_prefill_ragged(d, y, g, b, st, None, o, lens, 64, ws)
+                                     for _ in range(10)])
+    ms = time_graph(torch, graph, 2) / 10
     ntok = int(lengths.sum())
-    Cc, dd = 64, sh.DK
-    flops = (6 * dd * dd + 5 * Cc * dd + Cc * Cc / 3.0) * ntok * sh.HV
-    del y, g, b, o, ws
+    flops = prefill_flops(ntok, sh.HV, sh.DK)
+    byts = ntok * (C * 2 + 2 * sh.HV * 2 + sh.HV * sh.DV * 2) + 2 * sh.B * sh.HV * sh.DK * sh.DV * 4
+    attainable = min(BF16_MFMA_PEAK_TFLOPS, flops / byts * HBM_PEAK_GBS / 1e3)
+    tflops = flops / (ms / 1e3) / 1e12
+    del y, g, b, o, ws, graph
     torch.cuda.empty_cache()
     return dict(lengths=lengths.tolist(), call_ms=ms, tokens_per_s=ntok / (ms / 1e3),
-                achieved_tflops=flops / (ms / 1e3) / 1e12)
+                achieved_tflops=tflops, attainable_tflops=attainable,
+                frac_of_attainable=tflops / attainable)
 
 
-def gated_rmsnorm(torch, gb, W, args):
+def gated_rmsnorm(torch, gb, W, args, ceil):
     """The gated RMSNorm epilogue over the cohort's verify outputs (30 layers x
     8 rows x 2 tokens x 32 heads x 128, fp32 o, bf16 gate and weight, written
     in place), 10 launches captured in one HIP graph."""
@@ -606,23 +893,10 @@ def gated_rmsnorm(torch, gb, W, args):
     active = torch.from_numpy(act_rows).cuda()
     gb.gdn_gated_rmsnorm(d, o, z, w, o, active=active)
     torch.cuda.synchronize()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
     n = 10
-    with torch.cuda.graph(graph, stream=s):
-        for _ in range(n):
-            gb.gdn_gated_rmsnorm(d, o, z, w, o, active=active)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    tm = Timer(torch)
-    start = tm.ev()
-    for _ in range(5):
-        graph.replay()
-    end = tm.ev()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / (5 * n)
+    graph = graph_of(torch, lambda: [gb.gdn_gated_rmsnorm(d, o, z, w, o, active=active)
+                                     for _ in range(n)])
+    ms = time_graph(torch, graph, 5, warm=1) / n
     na = int(act_rows.sum())
     byts = L_POOL * na * sh.T * sh.HV * sh.DV * (4 + 2 + 4) + L_POOL * sh.DV * 2
     del o, z, graph
@@ -630,11 +904,13 @@ def gated_rmsnorm(torch, gb, W, args):
     return dict(ms_per_call=ms, bytes_per_call=byts, gbs=byts / (ms / 1e3) / 1e9)
 
 
-def verify_gated_norm(torch, gb, W, args):
+def verify_gated_norm(torch, gb, W, args, ceil):
     """Verify with the gated RMSNorm fused into its outputs
     (gdn_verify_gated_norm) against the same two steps as separate launches
-    (gdn_verify, then gdn_gated_rmsnorm in place), over the cohort's 30 layer
-    pools; 20 back-to-back launches of each between HIP events."""
+    (gdn_verify, then gdn_gated_rmsnorm in place), and the same for the fused
+    commit + verify, over the cohort's 30 layer pools.  Each variant is timed
+    twice, interleaved (20 back-to-back calls between HIP events each time),
+    and reported as the better of its two runs."""
     sh = W.COHORT
     big, t, rng, act_rows = cohort_pools(torch, W, sh, L_POOL, 1001)
     d = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
@@ -665,84 +941,46 @@ def verify_gated_norm(torch, gb, W, args):
         gb.gdn_gated_rmsnorm(d, t["o"], z, w, t["o"], active=t["active"])
 
     tm = Timer(torch)
-    res = {}
-    for name, fn in (("fused", fused), ("split", split), ("fused_again", fused),
-                     ("lazy_fused", lazy_fused), ("lazy_split", lazy_split)):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        reps = 20
-        a = tm.ev()
-        for _ in range(reps):
-            fn()
-        b = tm.ev()
-        torch.cuda.synchronize()
-        res[name] = a.elapsed_time(b) / reps
+    runs = {}
+    order = (("fused", fused), ("split", split), ("lazy_fused", lazy_fused),
+             ("lazy_split", lazy_split))
+    for _ in range(2):
+        for name, fn in order:
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            reps = 20
+            a = tm.ev()
+            for _ in range(reps):
+                fn()
+            b = tm.ev()
+            torch.cuda.synchronize()
+            runs.setdefault(name, []).append(a.elapsed_time(b) / reps)
     assert int(t["err"].item()) == 0, "device error word set"
     n_act = int(act_rows.sum())
     byts = verify_bytes(sh, n_act, L_POOL) + L_POOL * (n_act * sh.T * sh.HV * sh.DV * 2 + sh.DV * 2)
-    ms = min(res["fused"], res["fused_again"])
+    best = {k: min(v) for k, v in runs.items()}
     del t, z, w
     torch.cuda.empty_cache()
-    return dict(fused_ms=ms, split_ms=res["split"], bytes_per_call=byts,
-                gbs=byts / (ms / 1e3) / 1e9, lazy_fused_ms=res["lazy_fused"],
-                lazy_split_ms=res["lazy_split"])
+    return dict(fused_ms=best["fused"], split_ms=best["split"], bytes_per_call=byts,
+                gbs=byts / (best["fused"] / 1e3) / 1e9, lazy_fused_ms=best["lazy_fused"],
+                lazy_split_ms=best["lazy_split"], runs_ms=runs)
 
 
-def cpu_baseline(W, budget_s=12.0):
-    """The oracle as it stands (single-threaded C, float64) on a bounded
-    sample of the headline workload: whole verify + commit layer-cycles of
-    the B8/T2 cohort (8 rows x 32 heads each) until the time budget is used."""
-    import oracle
-    sh = W.COHORT
-    inp = W.verify_inputs(sh, seed=4242)
-    od = oracle.Dims(L=1, B=sh.B, T=sh.T, HV=sh.HV, HK=sh.HK, DK=sh.DK, DV=sh.DV, S=sh.S)
-    rng = np.random.default_rng(1)
-    st, cs, cur = inp["state"], inp["conv_state"], inp["cur"]
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        keep = W.keep_uniform(rng, sh, inp["active"])
-        st, _, _ = oracle.verify(od, inp["x"], inp["conv_w"], None, cs, inp["g"], inp["beta"],
-                                 st, cur, inp["active"])
-        cs, cur, _ = oracle.commit(od, inp["x"], cs, cur, keep, inp["active"])
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 400:
-            break
-    single = n * sh.B * sh.HV / el
+SECTIONS = {"per_layer": per_layer_cycle, "grouped": grouped_cycle, "lazy": lazy_legs,
+            "solo": solo, "rewind": rewind, "conv_step": conv_step, "prefill": prefill,
+            "prefill_ragged": prefill_ragged, "gated_rmsnorm": gated_rmsnorm,
+            "verify_gated_norm": verify_gated_norm, "ceilings": ceilings}
 
-    # The same oracle calls fanned out over the host's cores, one independent
-    # layer-cycle stream per thread (the C oracle runs outside the GIL).
-    import concurrent.futures as cf
-    workers = max(1, min(os.cpu_count() or 1, 16))
-    par_budget = budget_s * 0.75
+EXTRA = (("grouped_verify_commit_b8_t2_l30", "grouped"), ("lazy_commit_verify_b8_t2", "lazy"),
+         ("solo_b1_t3_l30", "solo"), ("rewind_b8_t4_l30", "rewind"),
+         ("conv_step_t1024", "conv_step"), ("prefill_b1_4096_in_1024_calls", "prefill"),
+         ("prefill_ragged_b8_up_to_1024", "prefill_ragged"),
+         ("gated_rmsnorm_b8_t2_l30", "gated_rmsnorm"),
+         ("verify_gated_norm_b8_t2_l30", "verify_gated_norm"))
 
-    def stream(seed):
-        r = np.random.default_rng(seed)
-        s_, c_, u_ = inp["state"].copy(), inp["conv_state"].copy(), inp["cur"].copy()
-        k = 0
-        t_end = time.perf_counter() + par_budget
-        while time.perf_counter() < t_end:
-            kp = W.keep_uniform(r, sh, inp["active"])
-            s_, _, _ = oracle.verify(od, inp["x"], inp["conv_w"], None, c_, inp["g"], inp["beta"],
-                                     s_, u_, inp["active"])
-            c_, u_, _ = oracle.commit(od, inp["x"], c_, u_, kp, inp["active"])
-            k += 1
-        return k
-
-    t1 = time.perf_counter()
-    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
-        counts = list(ex.map(stream, range(100, 100 + workers)))
-    el2 = time.perf_counter() - t1
-    return dict(value=single, unit="rows*heads/s", cores=1, kind="oracle",
-                sample="%d verify+commit layer-cycles of the B8/T2 cohort (8 rows x 32 heads, "
-                       "6 active) in %.1f s, single-threaded float64 C oracle incl. marshalling; "
-                       "host: %s, %d cpus" % (n, el, platform.processor() or platform.machine(),
-                                              os.cpu_count() or 0),
-                all_cores=dict(value=sum(counts) * sh.B * sh.HV / el2, cores=workers,
-                               sample="%d layer-cycles over %d threads in %.1f s, one independent "
-                                      "cycle stream per thread" % (sum(counts), workers, el2)))
+CPU_LEGS = {"solo_b1_t3_l30": cpu_solo, "rewind_b8_t4_l30": cpu_rewind,
+            "prefill_b1_4096_in_1024_calls": cpu_prefill}
 
 
 def main():
@@ -762,35 +1000,36 @@ def main():
         copy_probe(torch)
         return
     log("bench: %s on %s" % (gb.gdn_version(), torch.cuda.get_device_name(0)))
-    sections = {"per_layer_graph": per_layer_graph, "solo": solo, "rewind": rewind,
-                "conv_step": conv_step, "prefill": prefill, "lazy": lazy_cycle,
-                "prefill_ragged": prefill_ragged, "gated_rmsnorm": gated_rmsnorm,
-                "verify_gated_norm": verify_gated_norm}
     if args.only:
-        print(json.dumps({args.only: sections[args.only](torch, gb, W, args)}), flush=True)
+        ceil = {}
+        print(json.dumps({args.only: SECTIONS[args.only](torch, gb, W, args, ceil)}), flush=True)
         return
-    log("bench: headline B8/T2 cohort x %d layers, %d steps" % (L_POOL, args.steps))
-    h = headline(torch, gb, W, args)
-    log("bench: headline %.4f ms/step  verify %.1f GB/s" % (h["ms_per_step"], h["verify_gbs"]))
+    ceil = {}
+    if not args.only_headline:
+        log("bench: ceilings")
+        ceil = ceilings(torch, gb, W, args)
+        log("bench: ceilings -> %s" % json.dumps(ceil))
+    log("bench: headline B8/T2 cohort x %d layers, per-layer verify, %d steps" % (L_POOL, args.steps))
+    h = per_layer_cycle(torch, gb, W, args, ceil)
+    log("bench: headline %.4f ms/step  verify %.2f us/layer (%.1f GB/s)"
+        % (h["ms_per_step"], h["verify_ms_per_layer"] * 1e3, h["roofline"]["achieved"]))
     extra = {}
     if not args.only_headline:
-        for name, fn in (("lazy_commit_verify_b8_t2", lazy_cycle),
-                         ("per_layer_graph_b8_t2", per_layer_graph), ("solo_b1_t3_l30", solo),
-                         ("rewind_b8_t4", rewind), ("conv_step_t1024", conv_step),
-                         ("prefill_b1_4096_in_1024_calls", prefill),
-                         ("prefill_ragged_b8_up_to_1024", prefill_ragged),
-                         ("gated_rmsnorm_b8_t2_l30", gated_rmsnorm),
-                         ("verify_gated_norm_b8_t2_l30", verify_gated_norm)):
+        for name, key in EXTRA:
             log("bench: %s" % name)
-            extra[name] = fn(torch, gb, W, args)
+            extra[name] = SECTIONS[key](torch, gb, W, args, ceil)
             log("bench: %s -> %s" % (name, json.dumps(extra[name])))
+        extra["ceilings"] = ceil
     cpu = None
     if not args.no_cpu_baseline:
-        log("bench: cpu baseline (oracle)")
-        cpu = cpu_baseline(W)
-    vb = h["verify_bytes"]
-    log("bench: device copy rate")
-    copy_gbs = stream_copy_gbs(torch)
+        log("bench: cpu baselines (oracle)")
+        cpu = cpu_cohort(W, 10.0)
+        if not args.only_headline:
+            for name, fn in CPU_LEGS.items():
+                extra[name]["cpu_baseline"] = fn(W, 5.0)
+                log("bench: cpu %s -> %.1f %s" % (name, extra[name]["cpu_baseline"]["value"],
+                                                  extra[name]["cpu_baseline"]["unit"]))
+    roof = dict(h["roofline"])
     rec = {
         "metric": "GDN verify+commit rows*heads/s (B8,T2,32 heads) + achieved HBM GB/s vs peak",
         "value": h["value"],
@@ -805,23 +1044,19 @@ def main():
         "dtype": "fp32",
         "data": "synthetic",
         "config": {"workload": "qwen_verify_cohort_b8_t2_hv32_hk16_d128 x %d layer pools "
-                               "(grouped verify + grouped commit per cycle)" % L_POOL,
+                               "(per-layer verify, then one commit over all layers, per cycle)"
+                               % L_POOL,
                    "rows": 8, "active_rows": 6, "T": 2, "value_heads": 32, "qk_heads": 16,
                    "d_k": 128, "d_v": 128, "layers": L_POOL, "inputs": "bf16",
-                   "state": "fp32", "keep": "U{0,1,2} per cycle"},
-        "roofline": {"bound": "hbm", "kernel": "gdn::recurrent_kernel<128,128,bf16> (verify)",
-                     "achieved": h["verify_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": h["verify_gbs"] / HBM_PEAK_GBS,
-                     "traffic": counted_traffic("recurrent_kernel_verify_b8_t2_l30"),
-                     "algorithmic_bytes_per_launch": vb,
-                     "avg_launch_ms": h["verify_ms"],
-                     "stream_copy_gbs": copy_gbs,
-                     "frac_of_stream": h["verify_gbs"] / copy_gbs},
+                   "state": "fp32", "keep": "U{0,1,2} per cycle",
+                   "value_counts": "all 8 rows incl. the 2 inactive ones (see active_rows_heads_per_s)"},
+        "roofline": roof,
+        "active_rows_heads_per_s": h["active_rows_heads_per_s"],
         "cycle_gbs": h["cycle_gbs"],
         "algorithmic_min_bytes_per_cycle": h["algorithmic_min_bytes_per_cycle"],
         "algorithmic_min_gbs": h["algorithmic_min_gbs"],
-        "active_rows_heads_per_s": h["active_rows_heads_per_s"],
         "cpu_baseline": cpu,
+        "headline_detail": h,
         "extra": extra,
     }
     print(json.dumps(rec), flush=True)

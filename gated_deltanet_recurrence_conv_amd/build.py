@@ -3,7 +3,8 @@
     python -m gated_deltanet_recurrence_conv_amd.build
 
 Every HIP source under csrc/ is compiled and linked into one shared library
-next to this file.  Packed-fp32 VALU instructions are disabled on the device
+next to this file; the ceiling loops under ceiling/ (measurement
+infrastructure, not the path) go into a second one, libgdn_ceiling.so.  Packed-fp32 VALU instructions are disabled on the device
 (-packed-fp32-ops off); hipcc's host pass warns that it does not know that
 feature, which is harmless.  MFMA accumulators are kept in ordinary VGPRs
 where possible (-amdgpu-mfma-vgpr-form), so the fp32 state that the prefill
@@ -21,6 +22,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
+CEILING_SRC = os.path.join(HERE, "ceiling")
+CEILING_LIB = os.path.join(HERE, "libgdn_ceiling.so")
 ARCH = "gfx950"
 
 
@@ -31,27 +34,55 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-mcode-object-version=5", "-O3", "-std=c++17",
-           "-fPIC", "-shared",
-           "-Wall", "-Wno-unused-function",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-mllvm", "-amdgpu-mfma-vgpr-form",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp] + srcs
+FLAGS = ["--offload-arch=" + ARCH, "-mcode-object-version=5", "-O3", "-std=c++17", "-fPIC",
+         "-Wall", "-Wno-unused-function",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
+OBJDIR = os.path.join(HERE, "_build")
+
+
+def _run(cmd, verbose: bool) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in proc.stdout.splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)
     if proc.returncode != 0:
+        raise RuntimeError("hipcc failed (%d):\n%s" % (proc.returncode, out))
+    return out
+
+
+def _link(srcs, lib, incs, verbose: bool) -> str:
+    """Compiles each source to an object (in parallel), then links them."""
+    import concurrent.futures as cf
+    os.makedirs(OBJDIR, exist_ok=True)
+    inc_flags = []
+    for inc in incs:
+        inc_flags += ["-I", inc]
+    objs = [os.path.join(OBJDIR, os.path.splitext(os.path.basename(s))[0] + ".o") for s in srcs]
+    jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        outs = list(ex.map(lambda so: _run([hipcc()] + FLAGS + inc_flags + ["-c", so[0], "-o", so[1]],
+                                            verbose), zip(srcs, objs)))
+    tmp = lib + ".tmp%d" % os.getpid()
+    try:
+        outs.append(_run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose))
+    except RuntimeError:
         if os.path.exists(tmp):
             os.remove(tmp)
-        raise RuntimeError("hipcc failed (%d):\n%s" % (proc.returncode, out))
-    if out.strip() and verbose:
-        print(out)
-    os.replace(tmp, LIB)
+        raise
+    for out in outs:
+        if out.strip() and verbose:
+            print(out)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Builds libgdn.so and libgdn_ceiling.so; returns the path of libgdn.so."""
+    inc = os.path.join(ROOT, "include")
+    _link(sorted(glob.glob(os.path.join(CSRC, "*.hip"))), LIB, [inc, CSRC], verbose)
+    _link(sorted(glob.glob(os.path.join(CEILING_SRC, "*.hip"))), CEILING_LIB, [inc], verbose)
     return LIB
 
 

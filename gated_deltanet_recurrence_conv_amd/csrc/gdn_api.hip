@@ -1,9 +1,8 @@
 // gdn_api.hip -- the C ABI of libgdn.so: host-side validation, launch
-// geometry and status codes.  Every check runs before anything is launched
-// ("MTP inference: review and commit structure", Review fixes: grouped
-// replay checks all shapes, dtypes and devices before combining layers;
-// "Add request-owned eight-way MTP serving for Qwen 35B", Clean-install
-// verification: fail closed instead of falling back).  There is exactly one
+// geometry and status codes.  Every argument is validated before any launch,
+// and a call that fails validation launches nothing ("MTP inference: review
+// and commit structure", Review fixes; "Add request-owned eight-way MTP
+// serving for Qwen 35B", Clean-install verification).  There is exactly one
 // code path per call and no host fallback.
 #include "gdn.h"
 #include "gdn_internal.h"

@@ -54,69 +54,67 @@ __device__ __forceinline__ void store_vec8(void* base, size_t idx, int dt, const
 }
 
 // ---------------------------------------------------------------------------
-// Conv-window shift by keep tokens (commit and rewind).  grid =
-// (ceil(C / (8*256)), L*B); each thread handles 8 channels of one (layer,
-// row).  All three source rows are read into registers before the cache is
-// overwritten.
-__global__ __launch_bounds__(256) void window_kernel(WinParams p)
-{
-    const int lb = blockIdx.y;
-    const int b = lb % p.B;
-    const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+// Conv-window shift by keep tokens (commit and rewind).  One workgroup per
+// (layer, row); each thread moves 8 channels per pass.  Every thread reads the
+// row's status (keep, cur, active) before the workgroup barrier and the slot
+// is advanced by thread 0 only after it, so no thread reads cur while it is
+// being written.  All three source rows are read into registers before the
+// cache is overwritten.
+constexpr int WIN_THREADS = 512;
 
-    int shift;
-    {
-        const int kp = p.keep[b];
-        const int slot = p.cur ? p.cur[lb] : 0;
-        const bool act = p.mode == WIN_REWIND ? true : (p.active ? p.active[b] != 0 : true);
-        int e = 0;
-        if (kp < 0 || kp > p.T) e |= ERR_KEEP;
-        if (slot < 0 || slot >= p.S) e |= ERR_SLOT;
-        if (!act && kp != 0) e |= ERR_INACTIVE_KEEP;
-        if (e) {
-            if (blockIdx.x == 0 && threadIdx.x == 0 && p.err) atomicOr(p.err, e);
-            return;
-        }
-        if (!act || kp == 0) return;
-        // Only block 0 advances the slot.  Other blocks of this row read cur
-        // solely for the range check above, which the new value also passes.
-        if (p.mode == WIN_COMMIT && blockIdx.x == 0 && threadIdx.x == 0)
-            p.cur[lb] = (slot + kp) % p.S;
-        shift = kp;
+__global__ __launch_bounds__(WIN_THREADS) void window_kernel(WinParams p)
+{
+    const int lb = blockIdx.x;
+    const int b = lb % p.B;
+
+    const int kp = p.keep[b];
+    const int slot = p.cur ? p.cur[lb] : 0;
+    const bool act = p.mode == WIN_REWIND ? true : (p.active ? p.active[b] != 0 : true);
+    int e = 0;
+    if (kp < 0 || kp > p.T) e |= ERR_KEEP;
+    if (slot < 0 || slot >= p.S) e |= ERR_SLOT;
+    if (!act && kp != 0) e |= ERR_INACTIVE_KEEP;
+    __syncthreads();   // every read of cur[lb] precedes the write below
+    if (e) {
+        if (threadIdx.x == 0 && p.err) atomicOr(p.err, e);
+        return;
     }
-    if (c0 >= p.C) return;
+    if (!act || kp == 0) return;
+    if (p.mode == WIN_COMMIT && threadIdx.x == 0) p.cur[lb] = (slot + kp) % p.S;
+    const int shift = kp;
 
     const int esz = p.act == ACT_BF16 ? 2 : 4;
-    // Stage the three new rows: W[shift + r], r = 0..2.
-    uint4 buf[3][2];
+    for (int c0 = threadIdx.x * 8; c0 < p.C; c0 += 8 * WIN_THREADS) {
+        // Stage the three new rows: W[shift + r], r = 0..2.
+        uint4 buf[3][2];
 #pragma unroll
-    for (int r = 0; r < 3; ++r) {
-        const int q = shift + r;
-        const char* src;
-        if (q < 3)
-            src = static_cast<const char*>(p.conv_state) +
-                  ((static_cast<size_t>(lb) * 3 + q) * p.C + c0) * esz;
-        else
-            src = static_cast<const char*>(p.x) +
-                  ((static_cast<size_t>(lb) * p.T + (q - 3)) * p.C + c0) * esz;
-        buf[r][0] = reinterpret_cast<const uint4*>(src)[0];
-        if (esz == 4) buf[r][1] = reinterpret_cast<const uint4*>(src)[1];
-    }
+        for (int r = 0; r < 3; ++r) {
+            const int q = shift + r;
+            const char* src;
+            if (q < 3)
+                src = static_cast<const char*>(p.conv_state) +
+                      ((static_cast<size_t>(lb) * 3 + q) * p.C + c0) * esz;
+            else
+                src = static_cast<const char*>(p.x) +
+                      ((static_cast<size_t>(lb) * p.T + (q - 3)) * p.C + c0) * esz;
+            buf[r][0] = reinterpret_cast<const uint4*>(src)[0];
+            if (esz == 4) buf[r][1] = reinterpret_cast<const uint4*>(src)[1];
+        }
 #pragma unroll
-    for (int r = 0; r < 3; ++r) {
-        char* dst = static_cast<char*>(p.conv_state) + ((static_cast<size_t>(lb) * 3 + r) * p.C + c0) * esz;
-        reinterpret_cast<uint4*>(dst)[0] = buf[r][0];
-        if (esz == 4) reinterpret_cast<uint4*>(dst)[1] = buf[r][1];
+        for (int r = 0; r < 3; ++r) {
+            char* dst = static_cast<char*>(p.conv_state) + ((static_cast<size_t>(lb) * 3 + r) * p.C + c0) * esz;
+            reinterpret_cast<uint4*>(dst)[0] = buf[r][0];
+            if (esz == 4) reinterpret_cast<uint4*>(dst)[1] = buf[r][1];
+        }
     }
 }
 
 hipError_t launch_window(const WinParams& p, hipStream_t s)
 {
-    const int per_row = (p.C + 8 * 256 - 1) / (8 * 256);
     const long long rows = static_cast<long long>(p.L) * p.B;
-    if (rows > 65535 || rows <= 0) return hipErrorInvalidConfiguration;
+    if (rows > 0x7fffffffLL || rows <= 0) return hipErrorInvalidConfiguration;
     clear_stale_error();
-    hipLaunchKernelGGL(window_kernel, dim3(per_row, static_cast<unsigned>(rows)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(window_kernel, dim3(static_cast<unsigned>(rows)), dim3(WIN_THREADS), 0, s, p);
     return hipGetLastError();
 }
 

@@ -865,9 +865,12 @@ hipError_t launch_pf(const PrefillParams& p, hipStream_t s)
                        dim3(NTHR), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // One 16-column slice per workgroup while the grid fits the GPU in one
-    // round (the slice's chain sets the time); deeper grids put two slices
-    // of a head in each workgroup, whose output waves serve both.
+    // One 16-column slice per workgroup while there are no more one-slice
+    // workgroups than compute units (the slice's chain sets the time);
+    // larger grids put two slices of a head in each workgroup, whose output
+    // waves serve both.  The test is against the CU count, not against
+    // residency: a one-slice workgroup uses 412 VGPRs per lane in its state
+    // wave, so a CU holds one of them at a time.
     const long long groups = rows * p.HK;
     const long long blocks1 = (groups + 7) / 8 * 8 * (p.HV / p.HK) * (DV / 16);
     const int cus = device_cus();

@@ -15,8 +15,8 @@
  *  [P2] "MTP inference: review and commit structure" (eole docs):
  *       Functional commits items 2 and 4 (verifier buffers, accepted-prefix
  *       state replay, grouped copies, short convolution with a mutated
- *       convolution cache); Review fixes (grouped replay checks every shape,
- *       dtype and device before combining layers); Verification and limits
+ *       convolution cache); Review fixes (a grouped replay validates its
+ *       layers' arguments before combining them); Verification and limits
  *       (chunked recurrence differs from the sequential one only in rounding).
  *  [P3] "Add request-owned eight-way MTP serving for Qwen 35B" (MTPLX PR
  *       #245): What was broken item 2 (a row commits two, one or no tokens;

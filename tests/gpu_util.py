@@ -52,16 +52,19 @@ def dims_pair(sh, T=None, B=None, L=None, S=None, scale=1.0, flags=FLAGS, out=No
 
 def block_err(x, ref, block_axes) -> float:
     """Largest normwise error max|x - r| / max|r| over blocks; block_axes are
-    the axes that form one block (e.g. (-2, -1) for a state tile)."""
+    the axes that form one block (e.g. (-2, -1) for a state tile).  A block
+    whose reference is all zeros must be all zeros too: any nonzero (or NaN)
+    value there gives an infinite error."""
     x = np.asarray(x, np.float64)
     ref = np.asarray(ref, np.float64)
     assert x.shape == ref.shape, (x.shape, ref.shape)
-    num = np.max(np.abs(x - ref), axis=block_axes)
+    diff = np.abs(x - ref)
+    diff = np.where(np.isnan(diff), np.inf, diff)
+    num = np.max(diff, axis=block_axes)
     den = np.max(np.abs(ref), axis=block_axes)
-    ok = den > 0
-    if not np.any(ok):
-        return float(np.max(num))
-    return float(np.max(num[ok] / den[ok]))
+    zero = den == 0
+    rel = np.where(zero, np.where(num == 0, 0.0, np.inf), num / np.where(zero, 1.0, den))
+    return float(np.max(rel)) if rel.size else 0.0
 
 
 def state_err(x, ref) -> float:

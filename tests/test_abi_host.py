@@ -241,3 +241,35 @@ def test_status_strings_and_version(lib):
     for s in range(8):
         assert lib.gdn_status_string(s).startswith(b"GDN_")
     assert b"gfx950" in lib.gdn_version()
+
+
+CEILING_HEADER = os.path.join(ROOT, "include", "gdn_ceiling.h")
+CEILING_LIB = os.path.join(ROOT, "gated_deltanet_recurrence_conv_amd", "libgdn_ceiling.so")
+
+
+def test_ceiling_library_exports_its_header():
+    """libgdn_ceiling.so (the measured-ceiling loops) exports every function
+    include/gdn_ceiling.h declares, its binding has the same names, and it
+    refuses bad arguments with -1 before launching anything."""
+    if not os.path.exists(CEILING_LIB):
+        from gated_deltanet_recurrence_conv_amd import build
+        build.build()
+    text = open(CEILING_HEADER).read()
+    names = sorted(set(re.findall(r"^\s*int\s+(gdn_ceiling_\w+)\s*\(", text, re.M)))
+    assert names == ["gdn_ceiling_mfma_bf16", "gdn_ceiling_stream"]
+    clib = ctypes.CDLL(CEILING_LIB)
+    for n in names:
+        assert hasattr(clib, n), n
+    from gated_deltanet_recurrence_conv_amd import ceiling
+    for n in names:
+        assert hasattr(ceiling, n), n
+    vp = ctypes.c_void_p
+    clib.gdn_ceiling_stream.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_size_t, vp,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    clib.gdn_ceiling_mfma_bf16.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+    # too many buffers, no buffers, zero length, no sink for a read-only stream
+    assert clib.gdn_ceiling_stream(None, 3, None, 1, 16, None, 1, 4, 1, None) == -1
+    assert clib.gdn_ceiling_stream(None, 1, None, 1, 16, None, 1, 4, 1, None) == -1
+    assert clib.gdn_ceiling_stream(None, 0, None, 0, 0, None, 1, 4, 1, None) == -1
+    assert clib.gdn_ceiling_mfma_bf16(None, 1, 1, None) == -1
+    assert clib.gdn_ceiling_mfma_bf16(vp(16), 0, 1, None) == -1

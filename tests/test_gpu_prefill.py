@@ -294,19 +294,35 @@ def test_prefill_ragged_bad_length_reported():
     assert np.all(np.isfinite(o_g[:, 0, :50])) and np.all(np.isnan(o_g[:, 0, 50:]))
 
 
+def scan_slices_per_workgroup(rows, HV, HK, DV):
+    """The scan form the library launches: two 16-column slices per workgroup
+    when the one-slice grid (rows x qk heads padded to a multiple of 8, x
+    value heads per qk head x DV/16 slices) exceeds the GPU's compute units
+    and DV >= 32, else one."""
+    torch = torch_mod()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    groups = rows * HK
+    blocks1 = (groups + 7) // 8 * 8 * (HV // HK) * (DV // 16)
+    return 2 if DV >= 32 and blocks1 > cus else 1
+
+
 @pytest.mark.parametrize("DK,DV,lengths,out", [
     (128, 128, (200, 64, 1, 131), "f32"), (128, 128, (200, 64, 1, 131), "bf16"),
-    (64, 64, (70, 128, 5, 64), "f32"), (32, 32, (90, 1, 64, 65, 3, 128, 40, 7), "f32")])
+    (64, 64, (70, 128, 5, 64), "f32"), (32, 32, (90, 1, 64, 65, 3, 128, 40, 7), "f32"),
+    (128, 64, (150, 64, 3, 77, 12, 200, 1, 64), "f32"),
+    (64, 128, (100, 65, 2, 128), "f32"), (128, 32, (33, 1, 90, 64, 70, 5, 128, 10), "f32")])
 def test_prefill_two_slice_workgroups_equal_single_row_calls(DK, DV, lengths, out):
     """Ragged prompts at 32 value / 16 qk heads: 512 to 1,024 one-slice scan
     workgroups, more than the GPU holds at once, so the scan runs two column
-    slices per workgroup.  Each row equals a single-row call (256 or fewer
-    workgroups: one slice per workgroup) bit for bit, and the
-    token-sequential oracle within 2e-3."""
+    slices per workgroup (asserted from the device's compute-unit count).
+    Each row equals a single-row call (256 or fewer workgroups: one slice per
+    workgroup) bit for bit, and the token-sequential oracle within 2e-3."""
     torch = torch_mod()
     lengths = np.array(lengths, np.int32)
     T = int(lengths.max())
     nb = len(lengths)
+    assert scan_slices_per_workgroup(nb, 32, 16, DV) == 2
+    assert scan_slices_per_workgroup(1, 32, 16, DV) == 1
     sh = W.Shape("pf2", L=1, B=nb, T=T, HV=32, HK=16, DK=DK, DV=DV, S=2)
     inp = W.prefill_inputs(sh, seed=3700)
     inp["state"] = W.random_state(sh, seed=3701)
