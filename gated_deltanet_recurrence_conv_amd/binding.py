@@ -86,6 +86,7 @@ _lib.gdn_prefill_ragged.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                     ctypes.c_size_t, _vp, _vp]
 _lib.gdn_prefill_chunked.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                      ctypes.c_size_t, _vp, _vp]
+_lib.gdn_prefill_chunked_noalloc.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp]
 _lib.gdn_workspace_size.argtypes = [_D, _i32]
 _lib.gdn_workspace_size.restype = ctypes.c_size_t
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -96,13 +97,15 @@ _lib.gdn_last_hip_error.argtypes = []
 _lib.gdn_last_hip_error.restype = ctypes.c_char_p
 for _n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
            "gdn_accept_greedy", "gdn_gated_rmsnorm", "gdn_verify_gated_norm",
-           "gdn_verify_lazy_gated_norm", "gdn_prefill_chunked", "gdn_prefill_ragged"):
+           "gdn_verify_lazy_gated_norm", "gdn_prefill_chunked", "gdn_prefill_ragged",
+           "gdn_prefill_chunked_noalloc"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
             "gdn_accept_greedy", "gdn_gated_rmsnorm", "gdn_verify_gated_norm",
             "gdn_verify_lazy_gated_norm", "gdn_prefill_chunked", "gdn_prefill_ragged",
-            "gdn_workspace_size", "gdn_status_string", "gdn_version", "gdn_last_hip_error")
+            "gdn_prefill_chunked_noalloc", "gdn_workspace_size", "gdn_status_string", "gdn_version",
+            "gdn_last_hip_error")
 
 
 def _torch():
@@ -323,6 +326,23 @@ def gdn_prefill_chunked(d, y, g, beta, state, cur, o, chunk=64, workspace=None, 
         _arg(cur, "cur", s["cur"], torch.int32, True), _arg(o, "o", s["o"], O), int(chunk),
         ws_ptr, ws_bytes, _arg(err, "err", s["err"], torch.int32, True), _stream(stream)),
         "gdn_prefill_chunked")
+
+
+GDN_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gdn_prefill_chunked_noalloc(d, y, g, beta, state, cur, o, chunk=64, err=None, stream=None):
+    """gdn_prefill_chunked with the library's static device scratch in place of
+    a workspace (no allocation in the call); calls that overlap in time on one
+    GPU race."""
+    torch, s = _torch(), _shapes(d)
+    A, O = _act_dtype(d.act), _act_dtype(d.out)
+    _check(_lib.gdn_prefill_chunked_noalloc(
+        ctypes.byref(d), _arg(y, "y", s["x"], A), _arg(g, "g", s["g"], A),
+        _arg(beta, "beta", s["g"], A), _arg(state, "state", s["state"], torch.float32),
+        _arg(cur, "cur", s["cur"], torch.int32, True), _arg(o, "o", s["o"], O), int(chunk),
+        _arg(err, "err", s["err"], torch.int32, True), _stream(stream)),
+        "gdn_prefill_chunked_noalloc")
 
 
 def gdn_prefill_ragged(d, y, g, beta, state, cur, o, lengths, chunk=64, workspace=None, err=None,

@@ -9,6 +9,16 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
+// Device scratch of gdn_prefill_chunked_noalloc: the chunk records of the
+// prefill, in a static array of the library's code object instead of a
+// caller's workspace.  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never passes this name to a kernel (on the
+// host it is only a stand-in for the device symbol); it uses the device
+// address from hipGetSymbolAddress, kept per device.
+static __device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using gdn::RecParams;
@@ -77,6 +87,31 @@ gdn_status from_hip(hipError_t e)
     if (e == hipSuccess) return GDN_OK;
     g_last_hip_error = e;
     return GDN_E_HIP;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+gdn_status scratch_address(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return from_hip(e);
+    if (dev < 0 || dev >= 64) return GDN_E_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            gdn::clear_stale_error();
+            return from_hip(e != hipSuccess ? e : hipErrorInvalidSymbol);
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GDN_OK;
 }
 
 RecParams rec_params(const gdn_dims* d)
@@ -159,6 +194,36 @@ gdn_status verify_lazy_impl(const gdn_dims* d, const void* x_prev, const void* g
     w.active = nullptr; w.err = err; w.L = d->L; w.B = d->B; w.T = d->T; w.S = d->S;
     w.C = p.C; w.act = d->act; w.mode = gdn::WIN_REWIND;
     return from_hip(gdn::launch_window(w, s));
+}
+
+// Chunked prefill (padded or ragged).  With use_scratch the chunk records go
+// to the library's static device scratch instead of a caller's workspace;
+// dims whose records do not fit it are refused before anything is launched.
+gdn_status prefill_impl(const gdn_dims* d, const void* y, const void* g, const void* beta, float* state,
+                        const int32_t* cur, void* o, const int32_t* lengths, int32_t chunk, void* workspace,
+                        size_t workspace_bytes, bool use_scratch, int32_t* err, void* stream)
+{
+    gdn_status st = check_dims(d);
+    if (st != GDN_OK) return st;
+    if (chunk != 64) return GDN_E_SHAPE;
+    st = check_ptrs({y, g, beta, state, o}, {workspace}, {cur, lengths, err});
+    if (st != GDN_OK) return st;
+    if (!gdn::prefill_supported(d->DK, d->DV, d->act)) return GDN_E_UNSUPPORTED;
+    const size_t need = gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, chunk);
+    if (use_scratch) {
+        if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_E_WORKSPACE;
+        st = scratch_address(&workspace);
+        if (st != GDN_OK) return st;
+        workspace_bytes = GDN_NOALLOC_SCRATCH_BYTES;
+    }
+    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
+    gdn::PrefillParams p{};
+    p.y = y; p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.ws = workspace;
+    p.err = err; p.lengths = lengths;
+    p.L = d->L; p.B = d->B; p.T = d->T; p.HV = d->HV; p.HK = d->HK; p.S = d->S;
+    p.C = channels(d); p.act = d->act; p.out = d->out;
+    p.scale = d->scale; p.l2_eps = d->l2_eps; p.flags = d->flags;
+    return from_hip(gdn::launch_prefill(p, d->DK, d->DV, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -336,22 +401,17 @@ gdn_status gdn_prefill_ragged(const gdn_dims* d, const void* y, const void* g, c
                               int32_t chunk, void* workspace, size_t workspace_bytes, int32_t* err,
                               void* stream)
 {
-    gdn_status st = check_dims(d);
-    if (st != GDN_OK) return st;
-    if (chunk != 64) return GDN_E_SHAPE;
-    st = check_ptrs({y, g, beta, state, o}, {workspace}, {cur, lengths, err});
-    if (st != GDN_OK) return st;
-    if (!gdn::prefill_supported(d->DK, d->DV, d->act)) return GDN_E_UNSUPPORTED;
-    const size_t need = gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, chunk);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return GDN_E_WORKSPACE;
-    gdn::PrefillParams p{};
-    p.y = y; p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.ws = workspace;
-    p.err = err; p.lengths = lengths;
-    p.L = d->L; p.B = d->B; p.T = d->T; p.HV = d->HV; p.HK = d->HK; p.S = d->S;
-    p.C = channels(d); p.act = d->act; p.out = d->out;
-    p.scale = d->scale; p.l2_eps = d->l2_eps; p.flags = d->flags;
-    return from_hip(gdn::launch_prefill(p, d->DK, d->DV, static_cast<hipStream_t>(stream)));
+    return prefill_impl(d, y, g, beta, state, cur, o, lengths, chunk, workspace, workspace_bytes, false, err,
+                        stream);
 }
+
+gdn_status gdn_prefill_chunked_noalloc(const gdn_dims* d, const void* y, const void* g, const void* beta,
+                                       float* state, const int32_t* cur, void* o, int32_t chunk, int32_t* err,
+                                       void* stream)
+{
+    return prefill_impl(d, y, g, beta, state, cur, o, nullptr, chunk, nullptr, 0, true, err, stream);
+}
+
 
 gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* y, const void* g, const void* beta,
                                float* state, const int32_t* cur, void* o, int32_t chunk,

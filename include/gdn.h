@@ -259,6 +259,25 @@ gdn_status gdn_prefill_ragged(const gdn_dims* d, const void* y, const void* g, c
                               int32_t chunk, void* workspace, size_t workspace_bytes,
                               int32_t* err, void* stream);
 
+/* gdn_prefill_chunked without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the chunk records go to a static device
+ * array of the library, GDN_NOALLOC_SCRATCH_BYTES long, which every GPU the
+ * library runs on holds (its own copy) until the process ends.  The call
+ * allocates and frees nothing.  Dims whose records need more than that
+ * (gdn_workspace_size(d, chunk) > GDN_NOALLOC_SCRATCH_BYTES; e.g. one row of
+ * 1,024 tokens at 32 value heads and d = 128 needs 50,724,864 bytes) return
+ * GDN_E_WORKSPACE before anything is launched.  Every call on one GPU uses
+ * that GPU's one array: calls that overlap in time on the same GPU (other
+ * streams or threads) race and give undefined results; calls in one stream
+ * order are safe.  The records are written in full before they are read, so
+ * nothing carries over between calls.  Results equal gdn_prefill_chunked's
+ * bit for bit.  err: GDN_ERR_SLOT. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gdn_status gdn_prefill_chunked_noalloc(const gdn_dims* d, const void* y, const void* g,
+                                       const void* beta, float* state, const int32_t* cur, void* o,
+                                       int32_t chunk, int32_t* err, void* stream);
+
 /* Workspace bytes gdn_prefill_chunked needs for these dims (0 on bad dims). */
 size_t gdn_workspace_size(const gdn_dims* d, int32_t chunk);
 
