@@ -209,7 +209,7 @@ gdn_status prefill_impl(const gdn_dims* d, const void* y, const void* g, const v
     st = check_ptrs({y, g, beta, state, o}, {workspace}, {cur, lengths, err});
     if (st != GDN_OK) return st;
     if (!gdn::prefill_supported(d->DK, d->DV, d->act)) return GDN_E_UNSUPPORTED;
-    const size_t need = gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, chunk);
+    const size_t need = gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, d->act, chunk);
     if (use_scratch) {
         if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_E_WORKSPACE;
         st = scratch_address(&workspace);
@@ -337,7 +337,7 @@ gdn_status gdn_rewind(const gdn_dims* d, const void* x, const void* conv_w, cons
 size_t gdn_workspace_size(const gdn_dims* d, int32_t chunk)
 {
     if (check_dims(d) != GDN_OK || chunk != 64) return 0;
-    return gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, chunk);
+    return gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, d->act, chunk);
 }
 
 gdn_status gdn_verify_lazy(const gdn_dims* d, const void* x_prev, const void* g_prev,

@@ -145,8 +145,10 @@ struct NormParams {
 hipError_t launch_gated_rmsnorm(const NormParams& p, hipStream_t s);
 
 bool prefill_supported(int DK, int DV, int act);
-size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int chunk);
+size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int act, int chunk);
 hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s);
+// fp32 form of the chunked prefill (fp32 activations, d_k = 16): no workspace.
+hipError_t launch_prefill_f32(const PrefillParams& p, int DK, int DV, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Device helpers.

@@ -48,13 +48,13 @@
 // multiplying the row-major tile by a 0/1 selection matrix on the MFMA, which
 // is exact and lands the data in C layout, instead of 2-byte LDS transposes.
 #include "gdn_internal.h"
+#include "gdn_ut.h"
 
 namespace gdn {
 
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;      // chunk length
 constexpr int NTHR = 256;   // 4 waves
@@ -63,11 +63,6 @@ __device__ __forceinline__ f32x4 mfma(const uint4& a, const uint4& b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4 mfma32(float a, float b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 // hi = bf16(a), lo = bf16(a - hi), two values at a time (packed bf16x2)
@@ -123,25 +118,6 @@ __device__ __forceinline__ uint4 frag_from_c(const f32x4& lo, const f32x4& hi)
 {
     const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return cvt8(v);
-}
-
-// 16x16 block product on fp32 MFMA, operands in LDS with row pitches XP, YP
-// (floats): acc += X[xr.., xc..] * Y[yr.., yc..].
-template <int XP, int YP>
-__device__ __forceinline__ f32x4 blk_mul(const float* X, int xr, int xc, const float* Y, int yr, int yc,
-                                         f32x4 acc, int fr, int gq)
-{
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        acc = mfma32(X[(xr + fr) * XP + xc + 4 * kk + gq], Y[(yr + 4 * kk + gq) * YP + yc + fr], acc);
-    return acc;
-}
-
-template <int MP>
-__device__ __forceinline__ void blk_store(float* M, int r0, int c0, const f32x4& v, float sgn, int fr, int gq)
-{
-#pragma unroll
-    for (int j = 0; j < 4; ++j) M[(r0 + 4 * gq + j) * MP + c0 + fr] = sgn * v[j];
 }
 
 // ---------------------------------------------------------------------------
@@ -379,62 +355,9 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
     }
     lds_barrier();   // A complete
 
-    // ---- T = (I + A)^-1 on fp32 MFMA, 16x16 blocks by recursive doubling ----
-    {
-        float* S0 = &Scr[w][0][0][0];
-        float* S1 = &Scr[w][1][0][0];
-        // diagonal block w: (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8)
-        const int o = 16 * w;
-        f32x4 x;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            x[j] = ((fq + j) == fr ? 1.f : 0.f) - Af[(o + fq + j) * FP + o + fr];
-        blk_store<FP>(Tf, o, o, x, 1.f, fr, gq);
-        f32x4 pw = blk_mul<FP, FP>(Af, o, o, Af, o, o, f32x4{0.f, 0.f, 0.f, 0.f}, fr, gq);   // N^2
-        blk_store<SP>(S0, 0, 0, pw, 1.f, fr, gq);
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int step = 0; step < 3; ++step) {
-            float* Pcur = (step & 1) ? S1 : S0;
-            float* Pnext = (step & 1) ? S0 : S1;
-            x = blk_mul<FP, SP>(Tf, o, o, Pcur, 0, 0, x, fr, gq);      // X += X P
-            if (step < 2) pw = blk_mul<SP, SP>(Pcur, 0, 0, Pcur, 0, 0, f32x4{0.f, 0.f, 0.f, 0.f}, fr, gq);
-            __builtin_amdgcn_wave_barrier();
-            blk_store<FP>(Tf, o, o, x, 1.f, fr, gq);
-            if (step < 2) blk_store<SP>(Pnext, 0, 0, pw, 1.f, fr, gq);
-            __builtin_amdgcn_wave_barrier();
-        }
-    }
-    lds_barrier();
-    // off-diagonal 16x16 blocks of the two 32x32 halves: T10 = -D1 A10 D0, T32 = -D3 A32 D2
-    if (w == 1 || w == 3) {
-        const int b = 16 * (w - 1);   // column block of the pair
-        float* S0 = &Scr[w][0][0][0];
-        const f32x4 xa = blk_mul<FP, FP>(Af, b + 16, b, Tf, b, b, f32x4{0.f, 0.f, 0.f, 0.f}, fr, gq);
-        blk_store<SP>(S0, 0, 0, xa, 1.f, fr, gq);
-        __builtin_amdgcn_wave_barrier();
-        const f32x4 t = blk_mul<FP, SP>(Tf, b + 16, b + 16, S0, 0, 0, f32x4{0.f, 0.f, 0.f, 0.f}, fr, gq);
-        blk_store<FP>(Tf, b + 16, b, t, -1.f, fr, gq);
-    }
-    lds_barrier();
-    // lower-left 32x32 quadrant: X = A[32:64, 0:32] T[0:32, 0:32], then T21 = -T22 X.
-    // Block (pr, pc) of X lives in Scr[pr][pc].
-    {
-        const int pr = w >> 1, pc = w & 1;   // this wave's 16x16 block of X
-        f32x4 xa = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kb = pc; kb < 2; ++kb)   // T[0:32,0:32] is block lower triangular
-            xa = blk_mul<FP, FP>(Af, 32 + 16 * pr, 16 * kb, Tf, 16 * kb, 16 * pc, xa, fr, gq);
-        blk_store<SP>(&Scr[pr][pc][0][0], 0, 0, xa, 1.f, fr, gq);
-    }
-    lds_barrier();
-    {
-        const int pr = w >> 1, pc = w & 1;
-        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kb = 0; kb <= pr; ++kb)   // T[32:64, 32:64] is block lower triangular
-            t = blk_mul<FP, SP>(Tf, 32 + 16 * pr, 32 + 16 * kb, &Scr[kb][pc][0][0], 0, 0, t, fr, gq);
-        blk_store<FP>(Tf, 32 + 16 * pr, 16 * pc, t, -1.f, fr, gq);
-    }
-    lds_barrier();
+    // ---- T = (I + A)^-1 on fp32 MFMA (diagonal blocks by the product formula,
+    // then block substitution); ends with a workgroup barrier ----
+    ut_inverse64<FP>(Af, Tf, Scr, w, fr, gq);
 
     // ---- U~ = T diag(beta) V (split T) and W~^T = K^T (T diag(beta gamma / |k|))^T ----
     // Both read row r_me of T over the permuted token order.
@@ -920,15 +843,20 @@ size_t rec_bytes_dv(int DV)
 
 }  // namespace
 
+// The bf16 MFMA kernels serve bf16 activations with d_k >= 32; fp32
+// activations and d_k = 16 take the fp32 kernel (gdn_prefill_f32.hip).
+static bool bf16_path(int DK, int act) { return act == ACT_BF16 && DK >= 32; }
+
 bool prefill_supported(int DK, int DV, int act)
 {
-    return act == ACT_BF16 && (DK == 32 || DK == 64 || DK == 128) &&
+    return (act == ACT_BF16 || act == ACT_F32) && (DK == 16 || DK == 32 || DK == 64 || DK == 128) &&
            (DV == 16 || DV == 32 || DV == 64 || DV == 128);
 }
 
-size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int chunk)
+size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int act, int chunk)
 {
     if (chunk != CH) return 0;
+    if (!bf16_path(DK, act)) return 0;   // the fp32 kernel keeps everything in LDS
     size_t rec = 0;
     switch (DK) {
     case 32: rec = rec_bytes_dv<32>(DV); break;
@@ -942,6 +870,7 @@ size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int 
 
 hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s)
 {
+    if (!bf16_path(DK, p.act)) return launch_prefill_f32(p, DK, DV, s);
     switch (DK) {
     case 32: return launch_pf_dv<32>(p, DV, s);
     case 64: return launch_pf_dv<64>(p, DV, s);

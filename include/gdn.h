@@ -235,8 +235,12 @@ gdn_status gdn_verify_lazy_gated_norm(const gdn_dims* d, const void* x_prev, con
  * L2-normalised here when GDN_FLAG_QK_L2NORM is set.  Every row's state in
  * slot cur is advanced over all T tokens in place, and o[t] is written for
  * every token.  chunk must be 64; chunks restart at each call's first token
- * and the last one may be short.  workspace: device scratch of at least
- * gdn_workspace_size(d, chunk) bytes, owned by the caller, clobbered.
+ * and the last one may be short.  Every head shape (DK, DV in 16..128) and
+ * both activation dtypes are served: bf16 activations with DK >= 32 run on
+ * bf16 MFMA with fp32 accumulation (precision recovered by hi/lo splits),
+ * fp32 activations and DK = 16 on fp32 MFMA.  workspace: device scratch of
+ * at least gdn_workspace_size(d, chunk) bytes, owned by the caller,
+ * clobbered; may be NULL when that size is 0 (the fp32 form needs none).
  * err: GDN_ERR_SLOT. */
 gdn_status gdn_prefill_chunked(const gdn_dims* d, const void* y, const void* g,
                                const void* beta, float* state, const int32_t* cur, void* o,
@@ -278,7 +282,9 @@ gdn_status gdn_prefill_chunked_noalloc(const gdn_dims* d, const void* y, const v
                                        const void* beta, float* state, const int32_t* cur, void* o,
                                        int32_t chunk, int32_t* err, void* stream);
 
-/* Workspace bytes gdn_prefill_chunked needs for these dims (0 on bad dims). */
+/* Workspace bytes gdn_prefill_chunked and gdn_prefill_ragged need for these
+ * dims: 0 on bad dims and for the fp32 form (fp32 activations or DK = 16),
+ * which needs none. */
 size_t gdn_workspace_size(const gdn_dims* d, int32_t chunk);
 
 /* Static, human-readable name of a status. */

@@ -212,17 +212,30 @@ def test_conv_step_parity(T, out):
         assert np.all(np.abs(yg[:, a] - ref) <= np.abs(ref) * 2 ** -7 + 1e-30)
 
 
-def test_prefill_rejects_unsupported_and_small_workspace():
+def test_prefill_rejects_other_chunks_and_small_workspace():
+    """chunk != 64 is refused (GDN_E_SHAPE) and a workspace smaller than
+    gdn_workspace_size is refused before any launch; the fp32 form (d_k = 16
+    here) needs no workspace at all."""
     torch = torch_mod()
-    sh = W.Shape("pfx", L=1, B=1, T=64, HV=2, HK=1, DK=16, DV=16, S=1)
+    sh = W.Shape("pfx", L=1, B=1, T=64, HV=2, HK=1, DK=32, DV=16, S=1)
     d, _ = dims_pair(sh)
-    z = torch.zeros(64 * sh.C, dtype=torch.bfloat16, device="cuda")
-    st = torch.zeros(2 * 16 * 16, device="cuda")
-    o = torch.zeros(64 * 2 * 16, device="cuda")
-    gg = torch.zeros(64 * 2, dtype=torch.bfloat16, device="cuda")
+    need = B().gdn_workspace_size(d)
+    assert need > 0
+    z = torch.zeros((1, 1, 64, sh.C), dtype=torch.bfloat16, device="cuda")
+    st = torch.zeros((1, 1, 1, 2, 32, 16), device="cuda")
+    o = torch.full((1, 1, 64, 2, 16), float("nan"), device="cuda")
+    gg = torch.zeros((1, 1, 64, 2), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(B().GdnError) as ei:
-        B().gdn_prefill_chunked(d, z, gg, gg, st, None, o, 64, torch.zeros(1 << 20, dtype=torch.uint8, device="cuda"))
-    assert ei.value.status == 5   # d_k = 16 is not supported by the chunked kernels
+        B().gdn_prefill_chunked(d, z, gg, gg, st, None, o, 32,
+                                torch.zeros(need, dtype=torch.uint8, device="cuda"))
+    assert ei.value.status == 2
+    with pytest.raises(ValueError):
+        B().gdn_prefill_chunked(d, z, gg, gg, st, None, o, 64,
+                                torch.zeros(need - 16, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all()
+    d16, _ = dims_pair(sh.with_(DK=16))
+    assert B().gdn_workspace_size(d16) == 0
 
 
 def test_prefill_ragged_rows_equal_single_row_calls():
