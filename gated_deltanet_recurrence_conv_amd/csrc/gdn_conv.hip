@@ -126,13 +126,6 @@ hipError_t launch_window(const WinParams& p, hipStream_t s)
 // thread's loads are all in flight at once instead of one per token.
 constexpr int CONV_CT = 128;
 
-// SiLU with the hardware exp2 and reciprocal (each within about 1 ulp):
-// v * 1 / (1 + 2^(-v log2 e)).  Saturates to v and -0 at the extremes.
-__device__ __forceinline__ float silu_hw(float v)
-{
-    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
-}
-
 template <int ACT>
 __device__ __forceinline__ void to_f32x8(const uint4 (&raw)[ACT == ACT_BF16 ? 1 : 2], float* v)
 {

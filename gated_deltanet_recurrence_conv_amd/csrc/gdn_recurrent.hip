@@ -38,12 +38,15 @@ namespace gdn {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
+// Sum over the IG row groups of a wave (lanes JL apart); every lane ends
+// with the same bits.
 template <int IG, int JL>
 __device__ __forceinline__ float sum_over_rows(float v)
 {
-#pragma unroll
-    for (int off = JL; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    if constexpr (JL <= 4) v = xor_add<4>(v);
+    if constexpr (JL <= 8) v = xor_add<8>(v);
+    if constexpr (JL <= 16) v = xor_add<16>(v);
+    return xor_add<32>(v);
 }
 
 // One of four values chosen by a wave-uniform index (clamped to 0..3), so
@@ -76,25 +79,55 @@ constexpr int waves_per_head()
     return DV / (DV < 32 ? DV : 32);
 }
 
+#ifndef GDN_KSPLIT
+#define GDN_KSPLIT 1
+#endif
+// d_k parts of a (row, head, column slice): each part is one wave holding
+// DK / KS rows of the slice, and the partial d_k sums of a step are added
+// across the parts through LDS.  More waves per slice shortens each wave's
+// chain (loads, conv share, step arithmetic), which sets the time of a launch
+// that fits the GPU in one round (one layer of the B8/T2 cohort: 768 waves).
+// The split depends only on the head shape, so every mode and every batch
+// uses the same reduction tree.
+template <int DK, int DV>
+constexpr int ksplit()
+{
+    constexpr int SW = DV < 32 ? DV : 32;
+    constexpr int IG = 64 / (SW / 4);
+    return GDN_KSPLIT < DK / IG ? GDN_KSPLIT : DK / IG;
+}
+
+template <int DK, int DV, bool NORM>
+constexpr int waves_per_wg()
+{
+    return (NORM ? waves_per_head<DV>() : 1) * ksplit<DK, DV>();
+}
+
 template <int DK, int DV, int ACT, bool LAZY, bool NORM>
-__global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurrent_kernel(RecParams p)
+__global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent_kernel(RecParams p)
 {
     constexpr int SW = DV < 32 ? DV : 32;  // columns per wave
     constexpr int NS = DV / SW;            // column slices per head
     constexpr int JL = SW / 4;             // lanes across one row segment
     constexpr int IG = 64 / JL;            // row groups per wave
-    constexpr int RPL = DK / IG;           // rows held per lane
+    constexpr int KS = ksplit<DK, DV>();   // d_k parts (waves) per slice
+    constexpr int KR = DK / KS;            // rows of one part
+    constexpr int RPL = KR / IG;           // rows held per lane
     constexpr int MAXT = LAZY ? 8 : 4;     // tokens one wave runs
-    constexpr int NW = NORM ? NS : 1;      // waves per workgroup
+    constexpr int NW = NORM ? NS : 1;      // column slices per workgroup
+    constexpr int NWG = NW * KS;           // waves per workgroup
     // conv channels of the workgroup: q and k of the qk head, then the v
     // channels of its one slice, or (NORM) of all NS slices, whose waves share
     // the q and k conv
     constexpr int NCH = 2 * DK + (NORM ? DV : SW);
-    static_assert(RPL >= 1 && DK % IG == 0, "tile shape");
+    static_assert(RPL >= 1 && KR % IG == 0, "tile shape");
 
     __shared__ float ys[MAXT][NCH];
     __shared__ float ssq[NORM ? MAXT : 1][NW];   // per-slice sums of o^2 (NORM)
     __shared__ float gzw[NW][NORM ? 4 : 1][NORM ? SW : 1];   // w[j] * SiLU(z[t][j]) (NORM)
+    // partial d_k sums of a step (8 column sums, |q|^2, |k|^2, k.q) per part,
+    // double-buffered by step parity
+    __shared__ __align__(16) float xch[KS > 1 ? 2 : 1][NW][KS][JL][12];
 
     // ---- block -> (layer, row, qk head, value head, slice), XCD-aware ----
     const int bid = blockIdx.x;
@@ -107,11 +140,14 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
     const int lb = grp / p.HK;  // l * B + b
     const int b = lb % p.B;
     const int gsz = p.HV / p.HK;
-    const int wid = NORM ? static_cast<int>(threadIdx.x >> 6) : 0;
-    const int slice = NORM ? wid : r_in % NS;
+    const int wid = static_cast<int>(threadIdx.x >> 6);
+    const int kpart = wid % KS;            // d_k part of this wave
+    const int sw = wid / KS;               // slice wave index (NORM)
+    const int slice = NORM ? sw : r_in % NS;
     const int hv = NORM ? m * gsz + r_in : m * gsz + r_in / NS;
+    const int row0 = kpart * KR;           // first state row of this wave's part
 
-    const int lane = NORM ? static_cast<int>(threadIdx.x & 63) : static_cast<int>(threadIdx.x);
+    const int lane = static_cast<int>(threadIdx.x & 63);
     const int j4 = lane % JL;
     const int ig = lane / JL;
     const int col0 = slice * SW + j4 * 4;
@@ -160,8 +196,8 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
     const size_t srow = static_cast<size_t>(lb) * 3;          // conv_state row 0
     const bool has_bias = p.conv_b != nullptr;
     const void* bptr = has_bias ? p.conv_b : p.conv_w;
-    constexpr int NG = (NCH + 64 * NW - 1) / (64 * NW);   // channel groups per wave
-    // channel of group n in this lane: lane + 64 * (wid + NW * n)
+    constexpr int NG = (NCH + 64 * NWG - 1) / (64 * NWG);   // channel groups per wave
+    // channel of group n in this lane: lane + 64 * (wid + NWG * n)
     const int vcol = NORM ? 0 : slice * SW;   // first v column of the channel set
     constexpr int NROW = MAXT + 3;   // window rows per channel
     float wv[NG][4];
@@ -169,7 +205,7 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
     float bias[NG];
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
-        const int ch = min(lane + 64 * (wid + NW * n), NCH - 1);
+        const int ch = min(lane + 64 * (wid + NWG * n), NCH - 1);
         const int c = ch < DK ? m * DK + ch
                     : (ch < 2 * DK ? p.HK * DK + m * DK + (ch - DK)
                                    : 2 * p.HK * DK + hv * DV + vcol + (ch - 2 * DK));
@@ -244,30 +280,31 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
     f4 h[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
-        h[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src + (ig + IG * r) * DV));
+        h[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src + (row0 + ig + IG * r) * DV));
 
     // ---- conv + SiLU for every window token, into LDS ----
     const bool use_silu = (p.flags & FLAG_SILU) != 0;
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
-        const int ch = lane + 64 * (wid + NW * n);
+        const int ch = lane + 64 * (wid + NWG * n);
 #pragma unroll
         for (int t = 0; t < MAXT; ++t) {
-            float acc = wv[n][0] * win[n][t];
-            acc = fmaf(wv[n][1], win[n][t + 1], acc);
-            acc = fmaf(wv[n][2], win[n][t + 2], acc);
-            acc = fmaf(wv[n][3], win[n][t + 3], acc);
-            acc += bias[n];
-            const float sv = silu(acc);
-            if (ch < NCH && t < nsteps) ys[t][ch] = use_silu ? sv : acc;
+            if (t < nsteps) {   // wave-uniform
+                float acc = wv[n][0] * win[n][t];
+                acc = fmaf(wv[n][1], win[n][t + 1], acc);
+                acc = fmaf(wv[n][2], win[n][t + 2], acc);
+                acc = fmaf(wv[n][3], win[n][t + 3], acc);
+                acc += bias[n];
+                if (ch < NCH) ys[t][ch] = use_silu ? silu_hw(acc) : acc;
+            }
         }
     }
     if constexpr (NORM) {
-        if (ig == 0)
+        if (ig == 0 && kpart == 0)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) gzw[wid][t][j4 * 4 + c] = nw[c] * silu(zv[t][c]);
+                for (int c = 0; c < 4; ++c) gzw[sw][t][j4 * 4 + c] = nw[c] * silu_hw(zv[t][c]);
     }
     lds_barrier();
 
@@ -276,8 +313,8 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
         float kr[RPL], qr[RPL];
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
-            qr[r] = ys[t][ig + IG * r];
-            kr[r] = ys[t][DK + ig + IG * r];
+            qr[r] = ys[t][row0 + ig + IG * r];
+            kr[r] = ys[t][DK + row0 + ig + IG * r];
         }
         float pp[4] = {0.f, 0.f, 0.f, 0.f}, rr[4] = {0.f, 0.f, 0.f, 0.f};
         float sq = 0.f, sk = 0.f, kq = 0.f;
@@ -300,9 +337,37 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
         sq = sum_over_rows<IG, JL>(sq);
         sk = sum_over_rows<IG, JL>(sk);
         kq = sum_over_rows<IG, JL>(kq);
+        if constexpr (KS > 1) {
+            // add the parts' sums in part order, the same in every wave
+            float(*xs)[JL][12] = xch[t & 1][sw];
+            if (ig == 0) {
+                float* xp = xs[kpart][j4];
+                *reinterpret_cast<f4*>(xp) = f4{pp[0], pp[1], pp[2], pp[3]};
+                *reinterpret_cast<f4*>(xp + 4) = f4{rr[0], rr[1], rr[2], rr[3]};
+                *reinterpret_cast<f4*>(xp + 8) = f4{sq, sk, kq, 0.f};
+            }
+            lds_barrier();
+            f4 a0 = *reinterpret_cast<const f4*>(xs[0][j4]);
+            f4 a1 = *reinterpret_cast<const f4*>(xs[0][j4] + 4);
+            f4 a2 = *reinterpret_cast<const f4*>(xs[0][j4] + 8);
+#pragma unroll
+            for (int k = 1; k < KS; ++k) {
+                a0 += *reinterpret_cast<const f4*>(xs[k][j4]);
+                a1 += *reinterpret_cast<const f4*>(xs[k][j4] + 4);
+                a2 += *reinterpret_cast<const f4*>(xs[k][j4] + 8);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                pp[c] = a0[c];
+                rr[c] = a1[c];
+            }
+            sq = a2[0];
+            sk = a2[1];
+            kq = a2[2];
+        }
 
-        const float inv_nq = l2 ? 1.0f / sqrtf(sq + p.l2_eps) : 1.0f;
-        const float inv_nk = l2 ? 1.0f / sqrtf(sk + p.l2_eps) : 1.0f;
+        const float inv_nq = l2 ? __builtin_amdgcn_rsqf(sq + p.l2_eps) : 1.0f;
+        const float inv_nk = l2 ? __builtin_amdgcn_rsqf(sk + p.l2_eps) : 1.0f;
         const float kqn = kq * inv_nk * inv_nq;
         // t is uniform: select the token's gates without dynamic indexing.
         float gt, bt;
@@ -344,7 +409,7 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
                 for (int c = 1; c < 4; ++c) ss = fmaf(oo[c], oo[c], ss);
 #pragma unroll
                 for (int off = 1; off < JL; off <<= 1) ss += __shfl_xor(ss, off, 64);
-                if (lane == 0) ssq[t][wid] = ss;
+                if (lane == 0 && kpart == 0) ssq[t][sw] = ss;
                 lds_barrier();
                 float tot = ssq[t][0];
 #pragma unroll
@@ -352,7 +417,7 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
                 const float rn = 1.0f / sqrtf(tot / static_cast<float>(DV) + p.norm_eps);
                 const int tz = tout < 4 ? tout : 3;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) oo[c] = oo[c] * rn * gzw[wid][tz][j4 * 4 + c];
+                for (int c = 0; c < 4; ++c) oo[c] = oo[c] * rn * gzw[sw][tz][j4 * 4 + c];
             }
         }
         if (LAZY && t + 1 == kp) {
@@ -360,9 +425,9 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
             float* dst = st_lb + (static_cast<size_t>(slot0) * p.HV + hv) * tile + col0;
 #pragma unroll
             for (int r = 0; r < RPL; ++r)
-                __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(dst + (ig + IG * r) * DV));
+                __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(dst + (row0 + ig + IG * r) * DV));
         }
-        if (p.o && ig == 0 && tout >= 0) {
+        if (p.o && ig == 0 && kpart == 0 && tout >= 0) {
             const size_t oi = ((xrow + tout) * p.HV + hv) * DV + col0;
             if (p.out == ACT_BF16) {
                 uint2 pk;
@@ -379,44 +444,51 @@ __global__ __launch_bounds__(NORM ? 64 * waves_per_head<DV>() : 64) void recurre
             float* dst = st_lb + (static_cast<size_t>(slot) * p.HV + hv) * tile + col0;
 #pragma unroll
             for (int r = 0; r < RPL; ++r)
-                __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(dst + (ig + IG * r) * DV));
+                __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(dst + (row0 + ig + IG * r) * DV));
         }
     }
     if (!LAZY && p.mode == REC_REWIND) {
         float* dst = st_lb + (static_cast<size_t>(slot0) * p.HV + hv) * tile + col0;
 #pragma unroll
         for (int r = 0; r < RPL; ++r)
-            __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(dst + (ig + IG * r) * DV));
+            __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(dst + (row0 + ig + IG * r) * DV));
     }
 }
 
-// Occupancy cap for verify.  A verify wave streams its state slice in and its
-// candidates out with little arithmetic between; more than one such wave
-// resident per SIMD only adds concurrent DRAM streams and costs bandwidth
-// (measured at the B8/T2 cohort over 30 layers: one wave per SIMD 5.86 TB/s,
-// two 5.56, three 5.30).  The cap is set by reserving dynamic LDS so that
-// exactly wg_per_cu one-wave workgroups fit in a CU's LDS.  Rewind computes
-// up to T steps between its single read and single write of the slice and
-// needs the other waves to cover that, so it runs uncapped.
-constexpr int kVerifyWgPerCU = 4;   // one wave per SIMD
-// A verify grid many rounds deep (the 30-layer B8/T2 cohort: 30,720
-// workgroups, 30 rounds at four per CU) runs faster at five per CU once it is
-// streaming: in the decode loop (verify + commit replayed from a HIP graph)
-// 215-220 us per step against 227-236 us at four and 216-217 us at six, and
-// 203-205 us against 206-208 us for back-to-back verify launches (three
-// interleaved runs of each on one MI355X).  Short grids keep four: the solo
-// B1/T3 launch over 30 layers (3,840 workgroups) takes 56.9 us at four
-// against 58.7 us at five and 58.9 us at six.
-constexpr int kVerifyWgPerCULong = 5;
-constexpr int kVerifyLongRounds = 8;   // rounds at four per CU beyond which the long cap applies
-// Verify with the fused norm runs the NS waves of a head as one workgroup
-// with a barrier per token, so a wave stalls for its siblings; two such
-// workgroups per CU (two waves per SIMD) cover that (B8/T2 cohort, 30
-// layers: one per CU 253 us, two 204 us, three 203 us, uncapped 204 us,
-// against 216-224 us for verify plus the separate norm launch).
-constexpr int kVerifyNormWgPerCU = 2;
-constexpr int kRewindWgPerCU = 0;   // no cap
-constexpr int kLazyWgPerCU = 0;     // no cap (replay steps between read and write)
+// Occupancy caps, in waves per CU (a launch reserves dynamic LDS so that
+// cap / waves-per-workgroup workgroups fit in a CU's LDS).  A verify wave
+// streams its state slice in and its candidates out with little arithmetic
+// between; more than about one such wave resident per SIMD only adds
+// concurrent DRAM streams and costs bandwidth (measured with one-wave
+// workgroups at the B8/T2 cohort over 30 layers: one wave per SIMD 5.86 TB/s,
+// two 5.56, three 5.30).  A verify grid many rounds deep (the 30-layer
+// cohort) ran best at five waves per CU once streaming, shorter grids at
+// four.  Verify with the fused norm runs the waves of a head as one
+// workgroup with a barrier per token, so two waves per SIMD cover the
+// stalls.  Rewind and the fused commit + verify compute several steps
+// between their single read and write of the slice and need other waves to
+// cover that: they run uncapped (0).
+#ifndef GDN_VW_SHORT
+#define GDN_VW_SHORT 4
+#endif
+#ifndef GDN_VW_LONG
+#define GDN_VW_LONG 5
+#endif
+#ifndef GDN_VW_NORM
+#define GDN_VW_NORM 8
+#endif
+#ifndef GDN_VW_LAZY
+#define GDN_VW_LAZY 0
+#endif
+#ifndef GDN_VW_REWIND
+#define GDN_VW_REWIND 0
+#endif
+constexpr int kVerifyWavesPerCU = GDN_VW_SHORT;
+constexpr int kVerifyWavesPerCULong = GDN_VW_LONG;
+constexpr int kVerifyLongRounds = 8;   // rounds at the short cap beyond which the long cap applies
+constexpr int kVerifyNormWavesPerCU = GDN_VW_NORM;
+constexpr int kLazyWavesPerCU = GDN_VW_LAZY;
+constexpr int kRewindWavesPerCU = GDN_VW_REWIND;
 
 static size_t occupancy_lds_bytes(size_t static_bytes, int wg_per_cu)
 {
@@ -477,28 +549,30 @@ static hipError_t launch_rec(RecParams p, hipStream_t s)
 {
     constexpr int SW = DV < 32 ? DV : 32;
     constexpr int NS = DV / SW;
+    constexpr int KS = ksplit<DK, DV>();
     const bool lazy = p.mode == REC_LAZY;
     const bool norm = p.norm_w != nullptr;
-    const int nw = norm ? NS : 1;   // waves per workgroup
+    const int wpw = (norm ? NS : 1) * KS;   // waves per workgroup
     p.groups = p.L * p.B * p.HK;
     p.per_group = (p.HV / p.HK) * (norm ? 1 : NS);
     const long long blocks = static_cast<long long>((p.groups + 7) / 8) * 8 * p.per_group;
     if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    int cap = p.mode == REC_VERIFY ? kVerifyWgPerCU : p.mode == REC_LAZY ? kLazyWgPerCU : kRewindWgPerCU;
-    if (norm && nw > 1 && p.mode == REC_VERIFY) cap = kVerifyNormWgPerCU;
+    int waves = p.mode == REC_VERIFY ? kVerifyWavesPerCU : p.mode == REC_LAZY ? kLazyWavesPerCU : kRewindWavesPerCU;
+    if (norm && p.mode == REC_VERIFY) waves = kVerifyNormWavesPerCU;
     if (p.mode == REC_VERIFY && !norm) {
         const int cus = device_cus();
-        if (cus > 0 && blocks > static_cast<long long>(kVerifyLongRounds) * kVerifyWgPerCU * cus)
-            cap = kVerifyWgPerCULong;
+        if (cus > 0 && blocks * wpw > static_cast<long long>(kVerifyLongRounds) * kVerifyWavesPerCU * cus)
+            waves = kVerifyWavesPerCULong;
     }
+    const int cap = waves > 0 ? (waves / wpw > 0 ? waves / wpw : 1) : 0;   // workgroups per CU
     const dim3 grid(static_cast<unsigned>(blocks));
     clear_stale_error();
     if (lazy) {
-        if (norm) launch_rec_act<DK, DV, true, true>(p, grid, 64 * nw, cap, s);
-        else launch_rec_act<DK, DV, true, false>(p, grid, 64, cap, s);
+        if (norm) launch_rec_act<DK, DV, true, true>(p, grid, 64 * wpw, cap, s);
+        else launch_rec_act<DK, DV, true, false>(p, grid, 64 * wpw, cap, s);
     } else {
-        if (norm) launch_rec_act<DK, DV, false, true>(p, grid, 64 * nw, cap, s);
-        else launch_rec_act<DK, DV, false, false>(p, grid, 64, cap, s);
+        if (norm) launch_rec_act<DK, DV, false, true>(p, grid, 64 * wpw, cap, s);
+        else launch_rec_act<DK, DV, false, false>(p, grid, 64 * wpw, cap, s);
     }
     return hipGetLastError();
 }
