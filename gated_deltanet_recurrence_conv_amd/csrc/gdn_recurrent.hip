@@ -282,14 +282,16 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
     for (int r = 0; r < RPL; ++r)
         h[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src + (row0 + ig + IG * r) * DV));
 
-    // ---- conv + SiLU for every window token, into LDS ----
+    // ---- conv + SiLU for every window token, into LDS (a rewind without o
+    // needs no q channels) ----
     const bool use_silu = (p.flags & FLAG_SILU) != 0;
+    const int qskip = LAZY ? 0 : (p.mode == REC_REWIND && !p.o ? nsteps : 0);
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
         const int ch = lane + 64 * (wid + NWG * n);
 #pragma unroll
         for (int t = 0; t < MAXT; ++t) {
-            if (t < nsteps) {   // wave-uniform
+            if (t < nsteps && !(ch < DK && t < qskip)) {
                 float acc = wv[n][0] * win[n][t];
                 acc = fmaf(wv[n][1], win[n][t + 1], acc);
                 acc = fmaf(wv[n][2], win[n][t + 2], acc);
@@ -310,33 +312,52 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
 
     const bool l2 = (p.flags & FLAG_L2) != 0;
     for (int t = 0; t < nsteps; ++t) {
+        const int tout = LAZY ? t - kp : t;   // token of the window o belongs to
+        // A rewind without o needs neither h^T q nor |q| and k.q (a uniform
+        // branch; u and h are computed the same way in both).  The fused form
+        // keeps one step body for its replayed and verified tokens: with two
+        // (the replayed ones reduced like the rewind's) its 30-layer cohort
+        // cycle measured 171 against 148-152 us.
+        const bool want_out = p.o != nullptr && tout >= 0;
+        const bool full_step = LAZY || want_out;
         float kr[RPL], qr[RPL];
 #pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-            qr[r] = ys[t][row0 + ig + IG * r];
-            kr[r] = ys[t][DK + row0 + ig + IG * r];
-        }
+        for (int r = 0; r < RPL; ++r) kr[r] = ys[t][DK + row0 + ig + IG * r];
         float pp[4] = {0.f, 0.f, 0.f, 0.f}, rr[4] = {0.f, 0.f, 0.f, 0.f};
         float sq = 0.f, sk = 0.f, kq = 0.f;
+        if (full_step) {
 #pragma unroll
-        for (int r = 0; r < RPL; ++r) {
+            for (int r = 0; r < RPL; ++r) qr[r] = ys[t][row0 + ig + IG * r];
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    pp[c] = fmaf(h[r][c], kr[r], pp[c]);
+                    rr[c] = fmaf(h[r][c], qr[r], rr[c]);
+                }
+                sq = fmaf(qr[r], qr[r], sq);
+                sk = fmaf(kr[r], kr[r], sk);
+                kq = fmaf(kr[r], qr[r], kq);
+            }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                pp[c] = fmaf(h[r][c], kr[r], pp[c]);
-                rr[c] = fmaf(h[r][c], qr[r], rr[c]);
+                pp[c] = sum_over_rows<IG, JL>(pp[c]);
+                rr[c] = sum_over_rows<IG, JL>(rr[c]);
             }
-            sq = fmaf(qr[r], qr[r], sq);
-            sk = fmaf(kr[r], kr[r], sk);
-            kq = fmaf(kr[r], qr[r], kq);
-        }
+            sq = sum_over_rows<IG, JL>(sq);
+            sk = sum_over_rows<IG, JL>(sk);
+            kq = sum_over_rows<IG, JL>(kq);
+        } else {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            pp[c] = sum_over_rows<IG, JL>(pp[c]);
-            rr[c] = sum_over_rows<IG, JL>(rr[c]);
+            for (int r = 0; r < RPL; ++r) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) pp[c] = fmaf(h[r][c], kr[r], pp[c]);
+                sk = fmaf(kr[r], kr[r], sk);
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) pp[c] = sum_over_rows<IG, JL>(pp[c]);
+            sk = sum_over_rows<IG, JL>(sk);
         }
-        sq = sum_over_rows<IG, JL>(sq);
-        sk = sum_over_rows<IG, JL>(sk);
-        kq = sum_over_rows<IG, JL>(kq);
         if constexpr (KS > 1) {
             // add the parts' sums in part order, the same in every wave
             float(*xs)[JL][12] = xch[t & 1][sw];
@@ -366,9 +387,7 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
             kq = a2[2];
         }
 
-        const float inv_nq = l2 ? __builtin_amdgcn_rsqf(sq + p.l2_eps) : 1.0f;
         const float inv_nk = l2 ? __builtin_amdgcn_rsqf(sk + p.l2_eps) : 1.0f;
-        const float kqn = kq * inv_nk * inv_nq;
         // t is uniform: select the token's gates without dynamic indexing.
         float gt, bt;
         if constexpr (LAZY) {
@@ -385,12 +404,17 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
         }
         const float a = expf(gt);
 
-        float u[4], oo[4];
+        float u[4], oo[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const float vj = ys[t][2 * DK + (NORM ? slice * SW : 0) + j4 * 4 + c];
             u[c] = bt * (vj - a * (pp[c] * inv_nk));
-            oo[c] = p.scale * (a * (rr[c] * inv_nq) + u[c] * kqn);
+        }
+        if (want_out) {
+            const float inv_nq = l2 ? __builtin_amdgcn_rsqf(sq + p.l2_eps) : 1.0f;
+            const float kqn = kq * inv_nk * inv_nq;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) oo[c] = p.scale * (a * (rr[c] * inv_nq) + u[c] * kqn);
         }
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
@@ -399,9 +423,8 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
             for (int c = 0; c < 4; ++c) h[r][c] = fmaf(a, h[r][c], kn * u[c]);
         }
 
-        const int tout = LAZY ? t - kp : t;   // token of the window o belongs to
         if constexpr (NORM) {
-            if (tout >= 0) {   // uniform over the workgroup: kp is the row's
+            if (want_out) {   // uniform over the workgroup: kp is the row's
                 // every lane holds its row group's copy of the 4 columns; the
                 // JL lanes of a row group cover the wave's SW columns
                 float ss = oo[0] * oo[0];
@@ -427,7 +450,7 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
             for (int r = 0; r < RPL; ++r)
                 __builtin_nontemporal_store(h[r], reinterpret_cast<f4*>(dst + (row0 + ig + IG * r) * DV));
         }
-        if (p.o && ig == 0 && kpart == 0 && tout >= 0) {
+        if (want_out && ig == 0 && kpart == 0) {
             const size_t oi = ((xrow + tout) * p.HV + hv) * DV + col0;
             if (p.out == ACT_BF16) {
                 uint2 pk;
