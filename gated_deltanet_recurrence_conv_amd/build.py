@@ -86,5 +86,28 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(lib: str, verbose: bool = False) -> str:
+    """libgdn.so with the host code of the C ABI (gdn_api.hip: argument
+    validation, status codes, launch geometry) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer; device code and the other sources as in
+    build().  Each -fsanitize= applies to the host pass only (-Xarch_host).
+    The process that loads it must preload the clang sanitizer runtime."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = [os.path.join(OBJDIR, os.path.splitext(os.path.basename(s))[0] + ".o") for s in srcs]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    api = os.path.join(CSRC, "gdn_api.hip")
+    api_obj = lib + ".api.o"
+    _run([hipcc()] + FLAGS + inc + ["-g", "-fno-omit-frame-pointer",
+                                    "-Xarch_host", "-fsanitize=address",
+                                    "-Xarch_host", "-fsanitize=undefined",
+                                    "-Xarch_host", "-fno-sanitize-recover=all",
+                                    "-c", api, "-o", api_obj], verbose)
+    others = [o for s, o in zip(srcs, objs) if s != api]
+    _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", lib, api_obj] + others, verbose)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -12,7 +12,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gdn.h")
-LIB = os.path.join(ROOT, "gated_deltanet_recurrence_conv_amd", "libgdn.so")
+# GDN_LIB: another build of the library (the host sanitizer run)
+LIB = os.environ.get("GDN_LIB") or os.path.join(ROOT, "gated_deltanet_recurrence_conv_amd", "libgdn.so")
 
 
 @pytest.fixture(scope="module")
