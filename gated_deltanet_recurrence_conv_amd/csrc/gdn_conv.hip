@@ -60,7 +60,7 @@ __device__ __forceinline__ void store_vec8(void* base, size_t idx, int dt, const
 // is advanced by thread 0 only after it, so no thread reads cur while it is
 // being written.  All three source rows are read into registers before the
 // cache is overwritten.
-constexpr int WIN_THREADS = 512;
+constexpr int WIN_THREADS = 1024;
 
 __global__ __launch_bounds__(WIN_THREADS) void window_kernel(WinParams p)
 {
