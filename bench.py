@@ -235,8 +235,9 @@ def ceilings(torch, gb, W, args):
     """Sustained HBM rates of hand-written stream kernels for the read:write
     mixes of the path's kernels (read-only, write-only, copy 1:1, 1:2 as
     verify at T=2, 1:3 as verify at T=3, 2:1), each over buffers of 512 MiB
-    to 1 GiB, best over a small sweep of grid size, vectors per thread and
-    non-temporal vs plain access; and the dense bf16 MFMA rate of a loop of
+    to 1 GiB, best over a small sweep of grid size, vectors per thread,
+    non-temporal vs plain access and grid-stride vs per-workgroup contiguous
+    blocks; and the dense bf16 MFMA rate of a loop of
     independent v_mfma_f32_16x16x32_bf16 chains."""
     from gated_deltanet_recurrence_conv_amd import ceiling as ce
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -254,29 +255,32 @@ def ceilings(torch, gb, W, args):
         sink = torch.empty(cus * 64 * 4, dtype=torch.float32, device="cuda")
         srcs, dsts = bufs[:nr], bufs[nr:]
         best = (0.0, None)
-        for mult in (4, 8, 16):
-            for unroll in (2, 4, 8):
-                for nt in (True, False):
-                    grid = cus * mult
-                    if not dsts and grid * 4 > sink.numel():
-                        continue
+        configs = [(mult, unroll, nt, False) for mult in (4, 8, 16) for unroll in (2, 4, 8)
+                   for nt in (True, False)]
+        configs += [(mult, unroll, nt, True) for mult in (2, 4, 8) for unroll in (1, 2, 4)
+                    for nt in (True, False)]
+        for mult, unroll, nt, blocked in configs:
+            grid = cus * mult
+            if not dsts and grid * 4 > sink.numel():
+                continue
 
-                    def run():
-                        ce.gdn_ceiling_stream(srcs, dsts, n_vec, sink=sink, grid=grid,
-                                              unroll=unroll, nontemporal=nt)
-                    run()
-                    torch.cuda.synchronize()
-                    tm = Timer(torch)
-                    reps = 4
-                    a = tm.ev()
-                    for _ in range(reps):
-                        run()
-                    b = tm.ev()
-                    torch.cuda.synchronize()
-                    ms = a.elapsed_time(b) / reps
-                    gbs = n_vec * 16 * nbuf / (ms / 1e3) / 1e9
-                    if gbs > best[0]:
-                        best = (gbs, dict(grid_per_cu=mult, unroll=unroll, nontemporal=nt))
+            def run():
+                ce.gdn_ceiling_stream(srcs, dsts, n_vec, sink=sink, grid=grid,
+                                      unroll=unroll, nontemporal=nt, blocked=blocked)
+            run()
+            torch.cuda.synchronize()
+            tm = Timer(torch)
+            reps = 4
+            a = tm.ev()
+            for _ in range(reps):
+                run()
+            b = tm.ev()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / reps
+            gbs = n_vec * 16 * nbuf / (ms / 1e3) / 1e9
+            if gbs > best[0]:
+                best = (gbs, dict(grid_per_cu=mult, unroll=unroll, nontemporal=nt,
+                                  blocked=blocked))
         res[name + "_gbs"] = best[0]
         res[name + "_config"] = best[1]
         del bufs, sink
@@ -603,7 +607,8 @@ def lazy_legs(torch, gb, W, args, ceil):
 
     res = {}
     byts = float(np.mean([lazy_bytes(sh, keeps[i - 1], act_rows, L_POOL) for i in range(args.warmup, n)]))
-    for name, cyc, launches in (("per_layer", cycle_layers, 2 * L_POOL), ("grouped", cycle_grouped, 2)):
+    for name, cyc, launches, tkey in (("per_layer", cycle_layers, 2 * L_POOL, None),
+                                      ("grouped", cycle_grouped, 2, "lazy_b8_t2_l30")):
         for i in range(args.warmup):
             cyc(i)
         torch.cuda.synchronize()
@@ -623,7 +628,7 @@ def lazy_legs(torch, gb, W, args, ceil):
         gbs = byts / (ms / 1e3) / 1e9
         res[name] = dict(ms_per_cycle=ms, rows_heads_per_s=L_POOL * sh.B * sh.HV / (ms / 1e3),
                          bytes_per_cycle=byts, gbs=gbs, launches_per_cycle=launches,
-                         roofline=roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", None,
+                         roofline=roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", tkey,
                                            measured_peak=ceil.get("copy_gbs"),
                                            kernel="recurrent_kernel (lazy) + window_kernel, whole cycle"))
     del t
@@ -869,9 +874,58 @@ def prefill_ragged(torch, gb, W, args, ceil):
     tflops = flops / (ms / 1e3) / 1e12
     del y, g, b, o, ws, graph
     torch.cuda.empty_cache()
+    gbs = byts / (ms / 1e3) / 1e9
     return dict(lengths=lengths.tolist(), call_ms=ms, tokens_per_s=ntok / (ms / 1e3),
                 achieved_tflops=tflops, attainable_tflops=attainable,
-                frac_of_attainable=tflops / attainable)
+                frac_of_attainable=tflops / attainable, bytes_per_call=byts,
+                roofline=roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", "prefill_ragged_b8_t1024",
+                                  kernel="prefill_prep_kernel + prefill_scan_kernel, per call",
+                                  algorithmic_bytes_per_launch=byts, avg_launch_ms=ms,
+                                  achieved_tflops=tflops, attainable_tflops=attainable))
+
+
+def prefill_gated_norm(torch, gb, W, args, ceil):
+    """The gated RMSNorm after a 1,024-token prefill call (B1, 32 value / 16
+    qk heads, d = 128, bf16 in and out): the call alone against the call
+    followed by gdn_gated_rmsnorm over its outputs (o written in place), each
+    as 10 calls captured in one HIP graph.  The difference is the most a norm
+    fused into the prefill could save."""
+    sh = W.PREFILL
+    d = gb.make_dims(1, 1, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=1, act="bf16", out="bf16")
+    bf = torch.bfloat16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5012)
+    y = torch.randn((1, 1, sh.T, sh.C), generator=gen, device="cuda")
+    qk = y[..., :2 * sh.HK * sh.DK].reshape(1, 1, sh.T, 2 * sh.HK, sh.DK)
+    qk /= qk.norm(dim=-1, keepdim=True)
+    y = y.to(bf)
+    g = (-torch.nn.functional.softplus(torch.randn((1, 1, sh.T, sh.HV), generator=gen, device="cuda"))).to(bf)
+    b = torch.sigmoid(torch.randn((1, 1, sh.T, sh.HV), generator=gen, device="cuda")).to(bf)
+    z = torch.randn((1, 1, sh.T, sh.HV, sh.DV), generator=gen, device="cuda").to(bf)
+    w = (1.0 + 0.1 * torch.randn((1, sh.DV), generator=gen, device="cuda")).to(bf)
+    st = torch.zeros((1, 1, 1, sh.HV, sh.DK, sh.DV), device="cuda")
+    o = torch.empty((1, 1, sh.T, sh.HV, sh.DV), device="cuda", dtype=bf)
+    ws = torch.empty(gb.gdn_workspace_size(d), dtype=torch.uint8, device="cuda")
+
+    def call():
+        gb.gdn_prefill_chunked(d, y, g, b, st, None, o, 64, ws)
+
+    def call_norm():
+        call()
+        gb.gdn_gated_rmsnorm(d, o, z, w, o)
+
+    res = {}
+    for name, fn in (("prefill", call), ("prefill_then_norm", call_norm)):
+        fn()
+        torch.cuda.synchronize()
+        graph = graph_of(torch, lambda: [fn() for _ in range(10)])
+        res[name + "_ms"] = time_graph(torch, graph, 5) / 10
+        del graph
+    res["norm_ms"] = res["prefill_then_norm_ms"] - res["prefill_ms"]
+    res["norm_bytes"] = sh.T * sh.HV * sh.DV * 2 * 3 + sh.DV * 2
+    del y, g, b, z, o, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def gated_rmsnorm(torch, gb, W, args, ceil):
@@ -970,14 +1024,16 @@ def verify_gated_norm(torch, gb, W, args, ceil):
 SECTIONS = {"per_layer": per_layer_cycle, "grouped": grouped_cycle, "lazy": lazy_legs,
             "solo": solo, "rewind": rewind, "conv_step": conv_step, "prefill": prefill,
             "prefill_ragged": prefill_ragged, "gated_rmsnorm": gated_rmsnorm,
-            "verify_gated_norm": verify_gated_norm, "ceilings": ceilings}
+            "verify_gated_norm": verify_gated_norm, "prefill_gated_norm": prefill_gated_norm,
+            "ceilings": ceilings}
 
 EXTRA = (("grouped_verify_commit_b8_t2_l30", "grouped"), ("lazy_commit_verify_b8_t2", "lazy"),
          ("solo_b1_t3_l30", "solo"), ("rewind_b8_t4_l30", "rewind"),
          ("conv_step_t1024", "conv_step"), ("prefill_b1_4096_in_1024_calls", "prefill"),
          ("prefill_ragged_b8_up_to_1024", "prefill_ragged"),
          ("gated_rmsnorm_b8_t2_l30", "gated_rmsnorm"),
-         ("verify_gated_norm_b8_t2_l30", "verify_gated_norm"))
+         ("verify_gated_norm_b8_t2_l30", "verify_gated_norm"),
+         ("prefill_gated_norm_b1_t1024", "prefill_gated_norm"))
 
 CPU_LEGS = {"solo_b1_t3_l30": cpu_solo, "rewind_b8_t4_l30": cpu_rewind,
             "prefill_b1_4096_in_1024_calls": cpu_prefill}

@@ -34,8 +34,10 @@ def _check_dev(t, name):
         raise ValueError("%s must be a contiguous, 16-byte aligned GPU tensor" % name)
 
 
-def gdn_ceiling_stream(srcs, dsts, n_vec16, sink=None, grid=1024, unroll=4, nontemporal=True):
-    """Streams n_vec16 16-byte vectors from each tensor of srcs into each of dsts."""
+def gdn_ceiling_stream(srcs, dsts, n_vec16, sink=None, grid=1024, unroll=4, nontemporal=True,
+                       blocked=False):
+    """Streams n_vec16 16-byte vectors from each tensor of srcs into each of dsts
+    (grid-stride, or per-workgroup contiguous 64 KiB blocks when blocked)."""
     for i, t in enumerate(list(srcs) + list(dsts)):
         _check_dev(t, "buffer %d" % i)
         if t.numel() * t.element_size() < 16 * n_vec16:
@@ -50,7 +52,8 @@ def gdn_ceiling_stream(srcs, dsts, n_vec16, sink=None, grid=1024, unroll=4, nont
     dst_arr = (ctypes.c_void_p * 3)(*[t.data_ptr() for t in dsts], *([0] * (3 - len(dsts))))
     rc = _lib.gdn_ceiling_stream(src_arr, len(srcs), dst_arr, len(dsts), int(n_vec16),
                                  sink.data_ptr() if sink is not None else None, int(grid),
-                                 int(unroll), 1 if nontemporal else 0, _stream_ptr())
+                                 int(unroll), (1 if nontemporal else 0) | (2 if blocked else 0),
+                                 _stream_ptr())
     if rc != 0:
         raise RuntimeError("gdn_ceiling_stream failed (%d)" % rc)
 

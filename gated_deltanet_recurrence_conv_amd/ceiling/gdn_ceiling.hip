@@ -35,14 +35,21 @@ __device__ __forceinline__ void st(u4* p, u4 v)
     else *p = v;
 }
 
-// R read buffers, W write buffers, U vectors per thread per pass.
-template <int R, int W, int U, bool NT>
+// R read buffers, W write buffers, U vectors per thread per pass.  Grid
+// stride (BLK = 0): a pass of the grid covers nthr * U consecutive vectors.
+// Blocked (BLK > 0): workgroup g streams the contiguous blocks g, g + grid,
+// ... of BLK vectors, U vectors per thread per pass inside a block.
+template <int R, int W, int U, bool NT, int BLK>
 __global__ __launch_bounds__(256) void stream_kernel(StreamArgs a)
 {
-    const size_t tid = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-    const size_t nthr = static_cast<size_t>(gridDim.x) * 256;
+    const size_t tid = BLK ? threadIdx.x : static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    const size_t nthr = BLK ? 256 : static_cast<size_t>(gridDim.x) * 256;
     u4 acc = {0u, 0u, 0u, 0u};
-    for (size_t base = tid; base < a.n; base += nthr * U) {
+    const size_t nblk = BLK ? (a.n + BLK - 1) / BLK : 1;
+    for (size_t blk = BLK ? blockIdx.x : 0; blk < nblk; blk += BLK ? gridDim.x : 1) {
+    const size_t lo = BLK ? blk * BLK : 0;
+    const size_t hi = BLK ? (lo + BLK < a.n ? lo + BLK : a.n) : a.n;
+    for (size_t base = lo + tid; base < hi; base += nthr * U) {
         u4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) v[u] = u4{static_cast<uint32_t>(base), 1u, 2u, 3u};
@@ -52,7 +59,7 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs a)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const size_t i = base + u * nthr;
-                in[r][u] = i < a.n ? ld<NT>(a.src[r] + i) : u4{0u, 0u, 0u, 0u};
+                in[r][u] = i < hi ? ld<NT>(a.src[r] + i) : u4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -68,8 +75,9 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs a)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const size_t i = base + u * nthr;
-                if (i < a.n) st<NT>(a.dst[w] + i, v[u]);
+                if (i < hi) st<NT>(a.dst[w] + i, v[u]);
             }
+    }
     }
     if constexpr (W == 0) {
         // fold the workgroup's reads so that none of them is dead
@@ -84,34 +92,41 @@ __global__ __launch_bounds__(256) void stream_kernel(StreamArgs a)
     }
 }
 
+constexpr int kBlockVectors = 4096;   // 64 KiB per block in the blocked layout
+
 template <int R, int W, int U>
-hipError_t launch_stream_u(const StreamArgs& a, int grid, bool nt, hipStream_t s)
+hipError_t launch_stream_u(const StreamArgs& a, int grid, bool nt, bool blocked, hipStream_t s)
 {
-    if (nt) hipLaunchKernelGGL((stream_kernel<R, W, U, true>), dim3(grid), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((stream_kernel<R, W, U, false>), dim3(grid), dim3(256), 0, s, a);
+    if (blocked) {
+        if (nt) hipLaunchKernelGGL((stream_kernel<R, W, U, true, kBlockVectors>), dim3(grid), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((stream_kernel<R, W, U, false, kBlockVectors>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+        if (nt) hipLaunchKernelGGL((stream_kernel<R, W, U, true, 0>), dim3(grid), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((stream_kernel<R, W, U, false, 0>), dim3(grid), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
 template <int R, int W>
-hipError_t launch_stream_rw(const StreamArgs& a, int grid, int unroll, bool nt, hipStream_t s)
+hipError_t launch_stream_rw(const StreamArgs& a, int grid, int unroll, bool nt, bool blk, hipStream_t s)
 {
     switch (unroll) {
-    case 1: return launch_stream_u<R, W, 1>(a, grid, nt, s);
-    case 2: return launch_stream_u<R, W, 2>(a, grid, nt, s);
-    case 4: return launch_stream_u<R, W, 4>(a, grid, nt, s);
-    case 8: return launch_stream_u<R, W, 8>(a, grid, nt, s);
+    case 1: return launch_stream_u<R, W, 1>(a, grid, nt, blk, s);
+    case 2: return launch_stream_u<R, W, 2>(a, grid, nt, blk, s);
+    case 4: return launch_stream_u<R, W, 4>(a, grid, nt, blk, s);
+    case 8: return launch_stream_u<R, W, 8>(a, grid, nt, blk, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int R>
-hipError_t launch_stream_r(const StreamArgs& a, int W, int grid, int unroll, bool nt, hipStream_t s)
+hipError_t launch_stream_r(const StreamArgs& a, int W, int grid, int unroll, bool nt, bool blk, hipStream_t s)
 {
     switch (W) {
-    case 0: return launch_stream_rw<R, 0>(a, grid, unroll, nt, s);
-    case 1: return launch_stream_rw<R, 1>(a, grid, unroll, nt, s);
-    case 2: return launch_stream_rw<R, 2>(a, grid, unroll, nt, s);
-    case 3: return launch_stream_rw<R, 3>(a, grid, unroll, nt, s);
+    case 0: return launch_stream_rw<R, 0>(a, grid, unroll, nt, blk, s);
+    case 1: return launch_stream_rw<R, 1>(a, grid, unroll, nt, blk, s);
+    case 2: return launch_stream_rw<R, 2>(a, grid, unroll, nt, blk, s);
+    case 3: return launch_stream_rw<R, 3>(a, grid, unroll, nt, blk, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -149,7 +164,7 @@ bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 extern "C" {
 
 int gdn_ceiling_stream(const void* const* src, int n_read, void* const* dst, int n_write, size_t n_vec16,
-                       void* sink, int grid, int unroll, int nontemporal, void* stream)
+                       void* sink, int grid, int unroll, int mode, void* stream)
 {
     if (n_read < 0 || n_read > 2 || n_write < 0 || n_write > 3 || grid <= 0 || n_vec16 == 0) return -1;
     if ((n_read > 0 && !src) || (n_write > 0 && !dst) || (n_write == 0 && !sink)) return -1;
@@ -167,12 +182,13 @@ int gdn_ceiling_stream(const void* const* src, int n_read, void* const* dst, int
     a.n = n_vec16;
     (void)hipGetLastError();
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool nt = nontemporal != 0;
+    const bool nt = (mode & 1) != 0;
+    const bool blk = (mode & 2) != 0;
     hipError_t e;
     switch (n_read) {
-    case 0: e = launch_stream_r<0>(a, n_write, grid, unroll, nt, s); break;
-    case 1: e = launch_stream_r<1>(a, n_write, grid, unroll, nt, s); break;
-    default: e = launch_stream_r<2>(a, n_write, grid, unroll, nt, s); break;
+    case 0: e = launch_stream_r<0>(a, n_write, grid, unroll, nt, blk, s); break;
+    case 1: e = launch_stream_r<1>(a, n_write, grid, unroll, nt, blk, s); break;
+    default: e = launch_stream_r<2>(a, n_write, grid, unroll, nt, blk, s); break;
     }
     return e == hipSuccess ? 0 : static_cast<int>(e);
 }

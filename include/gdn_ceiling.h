@@ -27,10 +27,12 @@ extern "C" {
  * one 16-byte vector per workgroup into sink (at least grid vectors).  grid
  * workgroups of 256 threads walk the buffers with a stride of the whole grid;
  * each thread moves unroll (1, 2, 4 or 8) vectors per buffer per pass, all
- * loads of a pass issued before its stores.  Loads and stores are
- * non-temporal when nontemporal != 0. */
+ * loads of a pass issued before its stores.  mode bit 0: loads and stores
+ * are non-temporal; bit 1: blocked layout -- workgroup g streams the
+ * contiguous 64 KiB blocks g, g + grid, ... instead of the grid striding
+ * over the whole buffer. */
 int gdn_ceiling_stream(const void* const* src, int n_read, void* const* dst, int n_write,
-                       size_t n_vec16, void* sink, int grid, int unroll, int nontemporal,
+                       size_t n_vec16, void* sink, int grid, int unroll, int mode,
                        void* stream);
 
 /* Dense bf16 matrix-core loop: grid workgroups of 256 threads (4 waves); each
