@@ -185,10 +185,13 @@ gdn_status verify_lazy_impl(const gdn_dims* d, const void* x_prev, const void* g
     p.x_prev = keep_prev ? x_prev : x;
     p.g_prev = keep_prev ? g_prev : g;
     p.beta_prev = keep_prev ? beta_prev : beta;
-    st = from_hip(gdn::launch_recurrent(p, d->DK, d->DV, s));
-    if (st != GDN_OK || !keep_prev) return st;
-    // The conv cache is shifted by a second launch, after every wave has read
-    // the old cache.
+    p.conv_out = conv_state;
+    bool shifted = false;
+    st = from_hip(gdn::launch_recurrent(p, d->DK, d->DV, s, &shifted));
+    if (st != GDN_OK || !keep_prev || shifted) return st;
+    // Otherwise (the fused norm, or more waves per qk head than a workgroup
+    // holds) the conv cache is shifted by a second launch, after every wave
+    // has read the old cache.
     WinParams w{};
     w.x = x_prev; w.conv_state = conv_state; w.cur = const_cast<int32_t*>(cur); w.keep = keep_prev;
     w.active = nullptr; w.err = err; w.L = d->L; w.B = d->B; w.T = d->T; w.S = d->S;
@@ -323,10 +326,13 @@ gdn_status gdn_rewind(const gdn_dims* d, const void* x, const void* conv_w, cons
     p.x = x; p.conv_w = conv_w; p.conv_b = conv_b; p.conv_state = conv_state;
     p.g = g; p.beta = beta; p.state = state; p.cur = cur; p.o = o; p.active = nullptr;
     p.keep = keep; p.err = err; p.mode = gdn::REC_REWIND;
-    st = from_hip(gdn::launch_recurrent(p, d->DK, d->DV, s));
-    if (st != GDN_OK) return st;
-    // The conv cache is shifted by a second launch, after every wave of the
-    // replay has read the old cache.
+    p.conv_out = conv_state;
+    bool shifted = false;
+    st = from_hip(gdn::launch_recurrent(p, d->DK, d->DV, s, &shifted));
+    if (st != GDN_OK || shifted) return st;
+    // Otherwise (more waves per qk head than a workgroup holds) the conv cache
+    // is shifted by a second launch, after every wave of the replay has read
+    // the old cache.
     WinParams w{};
     w.x = x; w.conv_state = conv_state; w.cur = const_cast<int32_t*>(cur); w.keep = keep;
     w.active = nullptr; w.err = err; w.L = d->L; w.B = d->B; w.T = d->T; w.S = d->S;

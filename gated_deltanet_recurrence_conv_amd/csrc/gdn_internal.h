@@ -49,6 +49,8 @@ struct RecParams {
     const void* z;      // gated RMSNorm epilogue: gate input [L][B][T][HV][DV] (act)
     const void* norm_w; // and weight [L][DV] (act); null: o is written raw
     float norm_eps;
+    void* conv_out;     // lazy / rewind with one workgroup per qk head: the conv
+                        // cache (= conv_state) that the kernel itself shifts
 };
 
 // ---------------------------------------------------------------------------
@@ -104,7 +106,9 @@ inline int device_cus()
     return n;
 }
 
-hipError_t launch_recurrent(const RecParams& p, int DK, int DV, hipStream_t s);
+// *conv_shifted (if given) tells a lazy or rewind caller whether the launch
+// also shifted the conv cache (p.conv_out), so that no window launch follows.
+hipError_t launch_recurrent(const RecParams& p, int DK, int DV, hipStream_t s, bool* conv_shifted = nullptr);
 hipError_t launch_window(const WinParams& p, hipStream_t s);
 hipError_t launch_conv(const ConvParams& p, hipStream_t s);
 
@@ -185,6 +189,14 @@ __device__ __forceinline__ float load_act(const void* base, size_t idx)
 {
     if constexpr (ACT == ACT_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
     else return static_cast<const float*>(base)[idx];
+}
+
+// fp32 -> activation element (exact for a value that was loaded from it).
+template <int ACT>
+__device__ __forceinline__ void store_act(void* base, size_t idx, float v)
+{
+    if constexpr (ACT == ACT_BF16) static_cast<uint16_t*>(base)[idx] = f32_to_bf16_bits(v);
+    else static_cast<float*>(base)[idx] = v;
 }
 
 // Workgroup barrier over LDS only: waits for this wave's LDS accesses, then

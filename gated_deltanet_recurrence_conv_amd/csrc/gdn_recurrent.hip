@@ -97,14 +97,23 @@ constexpr int ksplit()
     return GDN_KSPLIT < DK / IG ? GDN_KSPLIT : DK / IG;
 }
 
-template <int DK, int DV, bool NORM>
+// GRP: one workgroup per (layer, row, qk head) holding the column-slice waves
+// of all its value heads (lazy and rewind).  Every conv channel of a row is
+// then read by exactly one lane of the launch, so that lane can write the
+// shifted conv cache itself, and the q/k conv is computed once per qk head
+// instead of once per wave.  At most kGroupMaxWaves waves per workgroup
+// (more than 8 would cap registers at 128 per lane and spill).
+constexpr int kGroupMaxWaves = 8;
+constexpr int kGroupGridWavesPerCU = 8;   // deepest grid that takes the GRP layout
+
+template <int DK, int DV, bool NORM, bool GRP>
 constexpr int waves_per_wg()
 {
-    return (NORM ? waves_per_head<DV>() : 1) * ksplit<DK, DV>();
+    return GRP ? kGroupMaxWaves : (NORM ? waves_per_head<DV>() : 1) * ksplit<DK, DV>();
 }
 
-template <int DK, int DV, int ACT, bool LAZY, bool NORM>
-__global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent_kernel(RecParams p)
+template <int DK, int DV, int ACT, bool LAZY, bool NORM, bool GRP>
+__global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM, GRP>())) void recurrent_kernel(RecParams p)
 {
     constexpr int SW = DV < 32 ? DV : 32;  // columns per wave
     constexpr int NS = DV / SW;            // column slices per head
@@ -114,13 +123,15 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
     constexpr int KR = DK / KS;            // rows of one part
     constexpr int RPL = KR / IG;           // rows held per lane
     constexpr int MAXT = LAZY ? 8 : 4;     // tokens one wave runs
-    constexpr int NW = NORM ? NS : 1;      // column slices per workgroup
-    constexpr int NWG = NW * KS;           // waves per workgroup
+    constexpr int NW = NORM ? NS : 1;      // column slices per workgroup (NORM)
+    constexpr int NWG = NW * KS;           // waves per workgroup (not GRP)
     // conv channels of the workgroup: q and k of the qk head, then the v
-    // channels of its one slice, or (NORM) of all NS slices, whose waves share
-    // the q and k conv
-    constexpr int NCH = 2 * DK + (NORM ? DV : SW);
+    // channels of its one slice, or (NORM) of all NS slices, or (GRP) of all
+    // slices of up to kGroupMaxWaves / NS value heads; its waves share the q
+    // and k conv (NCH is the LDS allocation, nch below the channels in use)
+    constexpr int NCH = 2 * DK + (GRP ? (kGroupMaxWaves / NS) * DV : NORM ? DV : SW);
     static_assert(RPL >= 1 && KR % IG == 0, "tile shape");
+    static_assert(!GRP || (KS == 1 && !NORM), "GRP workgroups hold whole slices, no norm");
 
     __shared__ float ys[MAXT][NCH];
     __shared__ float ssq[NORM ? MAXT : 1][NW];   // per-slice sums of o^2 (NORM)
@@ -133,8 +144,8 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
     const int bid = blockIdx.x;
     const int xcd = bid & 7;
     const int sgrp = bid >> 3;
-    const int r_in = sgrp % p.per_group;
-    const int grp = (sgrp / p.per_group) * 8 + xcd;
+    const int r_in = GRP ? 0 : sgrp % p.per_group;
+    const int grp = GRP ? bid : (sgrp / p.per_group) * 8 + xcd;
     if (grp >= p.groups) return;
     const int m = grp % p.HK;
     const int lb = grp / p.HK;  // l * B + b
@@ -143,8 +154,11 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
     const int wid = static_cast<int>(threadIdx.x >> 6);
     const int kpart = wid % KS;            // d_k part of this wave
     const int sw = wid / KS;               // slice wave index (NORM)
-    const int slice = NORM ? sw : r_in % NS;
-    const int hv = NORM ? m * gsz + r_in : m * gsz + r_in / NS;
+    const int slice = NORM ? sw : GRP ? wid % NS : r_in % NS;
+    const int hv = NORM ? m * gsz + r_in : GRP ? m * gsz + wid / NS : m * gsz + r_in / NS;
+    // waves and conv channels of the workgroup
+    const int nwg = GRP ? static_cast<int>(blockDim.x >> 6) : NWG;
+    const int nch = GRP ? 2 * DK + gsz * DV : NCH;
     const int row0 = kpart * KR;           // first state row of this wave's part
 
     const int lane = static_cast<int>(threadIdx.x & 63);
@@ -196,19 +210,19 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
     const size_t srow = static_cast<size_t>(lb) * 3;          // conv_state row 0
     const bool has_bias = p.conv_b != nullptr;
     const void* bptr = has_bias ? p.conv_b : p.conv_w;
-    constexpr int NG = (NCH + 64 * NWG - 1) / (64 * NWG);   // channel groups per wave
-    // channel of group n in this lane: lane + 64 * (wid + NWG * n)
-    const int vcol = NORM ? 0 : slice * SW;   // first v column of the channel set
+    // channel groups per wave (GRP: the most over 1 <= gsz, reached at gsz = 1)
+    constexpr int NG = GRP ? (2 * DK + DV + 64 * NS - 1) / (64 * NS) : (NCH + 64 * NWG - 1) / (64 * NWG);
+    // channel of group n in this lane: lane + 64 * (wid + nwg * n)
+    const int vch0 = GRP ? 2 * p.HK * DK + m * gsz * DV                    // all value heads of m
+                         : 2 * p.HK * DK + hv * DV + (NORM ? 0 : slice * SW);   // first v channel of the set
     constexpr int NROW = MAXT + 3;   // window rows per channel
     float wv[NG][4];
     float win[NG][NROW];
     float bias[NG];
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
-        const int ch = min(lane + 64 * (wid + NWG * n), NCH - 1);
-        const int c = ch < DK ? m * DK + ch
-                    : (ch < 2 * DK ? p.HK * DK + m * DK + (ch - DK)
-                                   : 2 * p.HK * DK + hv * DV + vcol + (ch - 2 * DK));
+        const int ch = min(lane + 64 * (wid + nwg * n), nch - 1);
+        const int c = ch < DK ? m * DK + ch : (ch < 2 * DK ? p.HK * DK + m * DK + (ch - DK) : vch0 + (ch - 2 * DK));
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             wv[n][j] = load_act<ACT>(p.conv_w, (static_cast<size_t>(l) * C + c) * 4 + j);
@@ -288,7 +302,7 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
     const int qskip = LAZY ? 0 : (p.mode == REC_REWIND && !p.o ? nsteps : 0);
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
-        const int ch = lane + 64 * (wid + NWG * n);
+        const int ch = lane + 64 * (wid + nwg * n);
 #pragma unroll
         for (int t = 0; t < MAXT; ++t) {
             if (t < nsteps && !(ch < DK && t < qskip)) {
@@ -297,7 +311,31 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
                 acc = fmaf(wv[n][2], win[n][t + 2], acc);
                 acc = fmaf(wv[n][3], win[n][t + 3], acc);
                 acc += bias[n];
-                if (ch < NCH) ys[t][ch] = use_silu ? silu_hw(acc) : acc;
+                if (ch < nch) ys[t][ch] = use_silu ? silu_hw(acc) : acc;
+            }
+        }
+    }
+    if constexpr (GRP) {
+        // A committing row's conv cache becomes window rows kp .. kp+2 of
+        // [conv cache ; tokens] (the replayed window's, in the fused form).
+        // This lane is the only reader of its channels in the whole launch,
+        // and it has read them: it can overwrite them now.  Lanes past the
+        // last channel re-read it and write nothing.
+        if (p.conv_out && kp > 0) {
+#pragma unroll
+            for (int n = 0; n < NG; ++n) {
+                const int ch = lane + 64 * (wid + nwg * n);
+                if (ch < nch) {
+                    const int c = ch < DK ? m * DK + ch
+                                : (ch < 2 * DK ? p.HK * DK + m * DK + (ch - DK) : vch0 + (ch - 2 * DK));
+#pragma unroll
+                    for (int r = 0; r < 3; ++r) {
+                        float v = win[n][1];   // kp + r is in 1 .. T + 2
+#pragma unroll
+                        for (int j = 2; j < NROW && j <= 6; ++j) v = kp + r == j ? win[n][j] : v;
+                        store_act<ACT>(p.conv_out, (srow + r) * C + c, v);
+                    }
+                }
             }
         }
     }
@@ -404,17 +442,20 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM>())) void recurrent
         }
         const float a = expf(gt);
 
+        // u and o are written with explicit fmaf so that no instantiation is
+        // left to contract them its own way: every mode and workgroup layout
+        // computes the same bits.
         float u[4], oo[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const float vj = ys[t][2 * DK + (NORM ? slice * SW : 0) + j4 * 4 + c];
-            u[c] = bt * (vj - a * (pp[c] * inv_nk));
+            const float vj = ys[t][2 * DK + (NORM ? slice * SW : GRP ? (wid / NS) * DV + slice * SW : 0) + j4 * 4 + c];
+            u[c] = bt * fmaf(-a, pp[c] * inv_nk, vj);
         }
         if (want_out) {
             const float inv_nq = l2 ? __builtin_amdgcn_rsqf(sq + p.l2_eps) : 1.0f;
             const float kqn = kq * inv_nk * inv_nq;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) oo[c] = p.scale * (a * (rr[c] * inv_nq) + u[c] * kqn);
+            for (int c = 0; c < 4; ++c) oo[c] = p.scale * fmaf(a, rr[c] * inv_nq, u[c] * kqn);
         }
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
@@ -534,14 +575,14 @@ static size_t occupancy_lds_bytes(size_t static_bytes, int wg_per_cu)
 // Static LDS of one kernel instantiation, queried once per process (the
 // cache is a static of this function template, so each instantiation has its
 // own).
-template <int DK, int DV, int ACT, bool LAZY, bool NORM>
+template <int DK, int DV, int ACT, bool LAZY, bool NORM, bool GRP>
 static size_t static_lds()
 {
     static std::atomic<long long> cached{-1};
     long long v = cached.load(std::memory_order_relaxed);
     if (v < 0) {
         hipFuncAttributes a{};
-        if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(recurrent_kernel<DK, DV, ACT, LAZY, NORM>)) !=
+        if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(recurrent_kernel<DK, DV, ACT, LAZY, NORM, GRP>)) !=
             hipSuccess) {
             clear_stale_error();
             return 0;   // no cap can be derived; the launch then runs uncapped
@@ -552,29 +593,56 @@ static size_t static_lds()
     return static_cast<size_t>(v);
 }
 
-template <int DK, int DV, int ACT, bool LAZY, bool NORM>
+template <int DK, int DV, int ACT, bool LAZY, bool NORM, bool GRP>
 static void launch_one(const RecParams& p, dim3 grid, int threads, int cap, hipStream_t s)
 {
-    const size_t st = cap > 0 ? static_lds<DK, DV, ACT, LAZY, NORM>() : 0;
+    const size_t st = cap > 0 ? static_lds<DK, DV, ACT, LAZY, NORM, GRP>() : 0;
     const size_t dyn = cap > 0 && st > 0 ? occupancy_lds_bytes(st, cap) : 0;
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT, LAZY, NORM>), grid, dim3(threads), dyn, s, p);
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT, LAZY, NORM, GRP>), grid, dim3(threads), dyn, s, p);
 }
 
-template <int DK, int DV, bool LAZY, bool NORM>
+template <int DK, int DV, bool LAZY, bool NORM, bool GRP = false>
 static void launch_rec_act(const RecParams& p, dim3 grid, int threads, int cap, hipStream_t s)
 {
-    if (p.act == ACT_BF16) launch_one<DK, DV, ACT_BF16, LAZY, NORM>(p, grid, threads, cap, s);
-    else launch_one<DK, DV, ACT_F32, LAZY, NORM>(p, grid, threads, cap, s);
+    if (p.act == ACT_BF16) launch_one<DK, DV, ACT_BF16, LAZY, NORM, GRP>(p, grid, threads, cap, s);
+    else launch_one<DK, DV, ACT_F32, LAZY, NORM, GRP>(p, grid, threads, cap, s);
 }
 
 template <int DK, int DV>
-static hipError_t launch_rec(RecParams p, hipStream_t s)
+static hipError_t launch_rec(RecParams p, hipStream_t s, bool* conv_shifted)
 {
     constexpr int SW = DV < 32 ? DV : 32;
     constexpr int NS = DV / SW;
     constexpr int KS = ksplit<DK, DV>();
     const bool lazy = p.mode == REC_LAZY;
     const bool norm = p.norm_w != nullptr;
+    // Lazy and rewind without the norm, on a grid the GPU holds at once (two
+    // waves per SIMD, e.g. one layer of the B8 cohort): one workgroup per qk
+    // head, which also shifts the conv cache, so no second launch follows.
+    // Deeper grids (all 30 layers in one launch) keep one-wave workgroups and
+    // the separate shift: there the 8-wave workgroups run one per CU and
+    // stream worse (30-layer cohort: fused cycle 162 against 151 us, rewind
+    // 166 against 156 us; one layer: 15.3 against 19.7 us per layer-cycle).
+    const int cus = device_cus();
+    const long long grp_waves = static_cast<long long>(p.L) * p.B * p.HV * NS;
+    const bool grp = (lazy || p.mode == REC_REWIND) && !norm && KS == 1 && p.conv_out != nullptr &&
+                     p.HK > 0 && (p.HV / p.HK) * NS <= kGroupMaxWaves && cus > 0 &&
+                     grp_waves <= static_cast<long long>(kGroupGridWavesPerCU) * cus;
+    if (conv_shifted) *conv_shifted = grp;
+    if (grp) {
+        const int wpw = (p.HV / p.HK) * NS;
+        p.groups = p.L * p.B * p.HK;
+        p.per_group = 1;
+        const long long blocks = static_cast<long long>(p.groups);
+        if (blocks <= 0 || blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        const int waves = lazy ? kLazyWavesPerCU : kRewindWavesPerCU;
+        const int cap = waves > 0 ? (waves / wpw > 0 ? waves / wpw : 1) : 0;
+        clear_stale_error();
+        if (lazy) launch_rec_act<DK, DV, true, false, true>(p, dim3(static_cast<unsigned>(blocks)), 64 * wpw, cap, s);
+        else launch_rec_act<DK, DV, false, false, true>(p, dim3(static_cast<unsigned>(blocks)), 64 * wpw, cap, s);
+        return hipGetLastError();
+    }
+    p.conv_out = nullptr;
     const int wpw = (norm ? NS : 1) * KS;   // waves per workgroup
     p.groups = p.L * p.B * p.HK;
     p.per_group = (p.HV / p.HK) * (norm ? 1 : NS);
@@ -601,24 +669,25 @@ static hipError_t launch_rec(RecParams p, hipStream_t s)
 }
 
 template <int DK>
-static hipError_t launch_rec_dv(const RecParams& p, int DV, hipStream_t s)
+static hipError_t launch_rec_dv(const RecParams& p, int DV, hipStream_t s, bool* cs)
 {
     switch (DV) {
-    case 16: return launch_rec<DK, 16>(p, s);
-    case 32: return launch_rec<DK, 32>(p, s);
-    case 64: return launch_rec<DK, 64>(p, s);
-    case 128: return launch_rec<DK, 128>(p, s);
+    case 16: return launch_rec<DK, 16>(p, s, cs);
+    case 32: return launch_rec<DK, 32>(p, s, cs);
+    case 64: return launch_rec<DK, 64>(p, s, cs);
+    case 128: return launch_rec<DK, 128>(p, s, cs);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_recurrent(const RecParams& p, int DK, int DV, hipStream_t s)
+hipError_t launch_recurrent(const RecParams& p, int DK, int DV, hipStream_t s, bool* conv_shifted)
 {
+    if (conv_shifted) *conv_shifted = false;
     switch (DK) {
-    case 16: return launch_rec_dv<16>(p, DV, s);
-    case 32: return launch_rec_dv<32>(p, DV, s);
-    case 64: return launch_rec_dv<64>(p, DV, s);
-    case 128: return launch_rec_dv<128>(p, DV, s);
+    case 16: return launch_rec_dv<16>(p, DV, s, conv_shifted);
+    case 32: return launch_rec_dv<32>(p, DV, s, conv_shifted);
+    case 64: return launch_rec_dv<64>(p, DV, s, conv_shifted);
+    case 128: return launch_rec_dv<128>(p, DV, s, conv_shifted);
     default: return hipErrorInvalidValue;
     }
 }

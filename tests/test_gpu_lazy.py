@@ -62,10 +62,25 @@ def lazy(r, bd, keep):
                         None, r.cs, r.g, r.b, r.state, r.cur, r.o, r.active, r.err)
 
 
-@pytest.mark.parametrize("shape", ["cohort", "rewind"])
+# Head shapes beyond the cohort's, fp32 (1e-5): value heads per qk head times
+# column slices per head sets how many waves a qk head's workgroup holds; the
+# last shape has more than one workgroup holds, so its conv cache is shifted by
+# a second launch.
+DIM_SHAPES = {
+    "cohort": W.COHORT,
+    "rewind": W.REWIND,
+    "d16_g2": W.Shape("d16_g2", L=2, B=3, T=3, HV=4, HK=2, DK=16, DV=16, S=4, act="f32", inactive=(1,)),
+    "k128_v16": W.Shape("k128_v16", L=2, B=3, T=3, HV=4, HK=2, DK=128, DV=16, S=4, act="f32", inactive=(1,)),
+    "k16_v128": W.Shape("k16_v128", L=2, B=3, T=4, HV=4, HK=2, DK=16, DV=128, S=5, act="f32"),
+    "g1_v64": W.Shape("g1_v64", L=2, B=3, T=2, HV=4, HK=4, DK=32, DV=64, S=4, act="f32", inactive=(2,)),
+    "g4_v128": W.Shape("g4_v128", L=2, B=3, T=3, HV=8, HK=2, DK=64, DV=128, S=4, act="f32"),
+}
+
+
+@pytest.mark.parametrize("shape", list(DIM_SHAPES))
 def test_lazy_equals_rewind_then_verify(shape):
-    sh = W.COHORT if shape == "cohort" else W.REWIND
-    prev, new, keep, cur = two_windows(sh, 5100 if shape == "cohort" else 5200)
+    sh = DIM_SHAPES[shape]
+    prev, new, keep, cur = two_windows(sh, 5100 + 100 * list(DIM_SHAPES).index(shape))
     active = new["active"]
     bd, od = dims_pair(sh)
     torch = torch_mod()
@@ -85,12 +100,13 @@ def test_lazy_equals_rewind_then_verify(shape):
     assert np.array_equal(host(ra.cur), cur)
     oa, ob = host(ra.o), host(rb.o)
     for b in range(sh.B):
-        c0 = int(cur[0, b])
-        assert np.array_equal(sa[:, b, c0], sb[:, b, c0])
-        others = [s for s in range(sh.S) if s != c0]
-        assert np.array_equal(sa[:, b, others], snap[:, b, others])   # no candidates
-        if keep[b] == 0:
-            assert np.array_equal(sa[:, b, c0], snap[:, b, c0])
+        for l in range(sh.L):
+            c0 = int(cur[l, b])
+            assert np.array_equal(sa[l, b, c0], sb[l, b, c0])
+            others = [s for s in range(sh.S) if s != c0]
+            assert np.array_equal(sa[l, b, others], snap[l, b, others])   # no candidates
+            if keep[b] == 0:
+                assert np.array_equal(sa[l, b, c0], snap[l, b, c0])
         if active[b]:
             assert np.array_equal(oa[:, b], ob[:, b])
         else:
@@ -104,8 +120,9 @@ def test_lazy_equals_rewind_then_verify(shape):
     assert e2 == 0
     assert np.array_equal(host(ra.cs).astype(np.float64), cs1)
     for b in range(sh.B):
-        c0 = int(cur[0, b])
-        assert state_err(sa[:, b, c0], st1[:, b, c0]) <= tol(sh.act)
+        for l in range(sh.L):
+            c0 = int(cur[l, b])
+            assert state_err(sa[l, b, c0], st1[l, b, c0]) <= tol(sh.act)
         if active[b]:
             assert out_err(oa[:, b:b + 1], o2[:, b:b + 1]) <= tol(sh.act)
 

@@ -210,6 +210,52 @@ def test_rewind_b8_t4_parity_and_equals_candidate():
         assert np.array_equal(st_gpu[:, b, others], snap[:, b, others])
 
 
+@pytest.mark.parametrize("DK,DV,HV,HK", [(16, 16, 4, 2), (128, 16, 4, 2), (16, 128, 4, 2),
+                                         (32, 64, 4, 4), (64, 128, 8, 2), (128, 128, 2, 1)])
+def test_rewind_head_shapes_fp32(DK, DV, HV, HK):
+    """Rewind over head shapes and value heads per qk head (fp32, 1e-5), with
+    and without outputs: the state, conv cache and outputs against the oracle,
+    and the two runs' states and caches bit-identical.  (64, 128, 8, 2) needs
+    more waves per qk head than one workgroup holds (the conv cache is then
+    shifted by a second launch)."""
+    sh = W.Shape("rw_dims", L=2, B=4, T=4, HV=HV, HK=HK, DK=DK, DV=DV, S=3, act="f32")
+    inp = W.verify_inputs(sh, seed=1300 + DK + DV + HV)
+    rng = np.random.default_rng(DK + DV + HV)
+    keep = np.array([0, 1, sh.T, 2], np.int32)
+    inp["cur"] = rng.integers(0, sh.S, size=(sh.L, sh.B)).astype(np.int32)
+    bd, od = dims_pair(sh, scale=DK ** -0.5)
+    st_ref, cs_ref, o_ref, err = oracle.rewind(od, inp["x"], inp["conv_w"], None,
+                                               inp["conv_state"], inp["g"], inp["beta"],
+                                               inp["state"], inp["cur"], keep)
+    assert err == 0
+    runs = []
+    for with_o in (True, False):
+        r = Run(sh, inp)
+        B().gdn_rewind(bd, r.x, r.w, None, r.cs, r.g, r.beta, r.state, r.cur, dev(keep),
+                       r.o if with_o else None, r.err)
+        torch_mod().cuda.synchronize()
+        assert int(host(r.err)[0]) == 0
+        runs.append(r)
+        assert np.array_equal(host(r.cs).astype(np.float64), cs_ref)
+        st = host(r.state)
+        for b in range(sh.B):
+            c0 = inp["cur"][:, b]
+            for l in range(sh.L):
+                if keep[b] == 0:
+                    assert np.array_equal(st[l, b], inp["state"][l, b])
+                else:
+                    assert state_err(st[l, b, c0[l]], st_ref[l, b, c0[l]]) <= 1e-5
+        if with_o:
+            o = host(r.o)
+            for b in range(sh.B):
+                k = int(keep[b])
+                if k:
+                    assert out_err(o[:, b:b + 1, :k], o_ref[:, b:b + 1, :k]) <= 1e-5
+                assert np.all(np.isnan(o[:, b, k:]))
+    assert np.array_equal(host(runs[0].state), host(runs[1].state))
+    assert np.array_equal(host(runs[0].cs), host(runs[1].cs))
+
+
 @pytest.mark.parametrize("DK,DV", [(16, 16), (16, 32), (32, 16), (32, 64), (64, 32),
                                    (64, 128), (128, 64), (128, 16), (16, 128)])
 def test_head_dims_fp32(DK, DV):
