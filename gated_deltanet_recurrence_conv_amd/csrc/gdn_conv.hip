@@ -260,11 +260,13 @@ hipError_t launch_conv_tr(const ConvParams& p, hipStream_t s)
     return hipGetLastError();
 }
 
-// Short windows (decode) use 4 tokens per thread, long ones (prefill) 8: at
-// 1,024 tokens and 8,192 channels that is 1,024 workgroups of two waves.
+// 4 tokens per thread at every window length (at least 3, so that only the
+// first token tile reads the old cache): at 1,024 tokens and 8,192 channels
+// 2,048 workgroups of two waves.  Measured there: 10.7 us per call against
+// 11.7 with 8 tokens per thread and 15.7 with 16.
 hipError_t launch_conv(const ConvParams& p, hipStream_t s)
 {
-    return p.T <= 8 ? launch_conv_tr<4>(p, s) : launch_conv_tr<8>(p, s);
+    return launch_conv_tr<4>(p, s);
 }
 
 }  // namespace gdn
