@@ -884,6 +884,54 @@ def prefill_ragged(torch, gb, W, args, ceil):
                                   achieved_tflops=tflops, attainable_tflops=attainable))
 
 
+def conv_prefill(torch, gb, W, args, ceil):
+    """The prompt path from the raw projection: B1 4,096-token prompts in
+    1,024-token calls (32 value / 16 qk heads, d = 128, bf16 in and out),
+    gdn_prefill_conv_chunked against gdn_conv_step + gdn_prefill_chunked,
+    each as the calls of 10 prompt buffers captured in one HIP graph (the
+    state and conv cache run on across them)."""
+    sh = W.PREFILL
+    nb, calls = 10, W.PREFILL_TOKENS // sh.T
+    C = sh.C
+    d = gb.make_dims(1, 1, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=1, act="bf16", out="bf16")
+    bf = torch.bfloat16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5013)
+    xs = [(torch.randn((calls, 1, 1, sh.T, C), generator=gen, device="cuda")).to(bf) for _ in range(nb)]
+    gs = [(-torch.nn.functional.softplus(torch.randn((calls, 1, 1, sh.T, sh.HV), generator=gen,
+                                                     device="cuda"))).to(bf) for _ in range(nb)]
+    bs = [torch.sigmoid(torch.randn((calls, 1, 1, sh.T, sh.HV), generator=gen, device="cuda")).to(bf)
+          for _ in range(nb)]
+    w = (0.5 * torch.randn((1, C, 4), generator=gen, device="cuda")).to(bf)
+    cs = torch.zeros((1, 1, 3, C), device="cuda", dtype=bf)
+    st = torch.zeros((1, 1, 1, sh.HV, sh.DK, sh.DV), device="cuda")
+    o = torch.empty((1, 1, sh.T, sh.HV, sh.DV), device="cuda", dtype=bf)
+    y = torch.empty((1, 1, sh.T, C), device="cuda", dtype=bf)
+    ws = torch.empty(gb.gdn_workspace_size(d), dtype=torch.uint8, device="cuda")
+
+    def fused(i, c):
+        gb.gdn_prefill_conv_chunked(d, xs[i][c], w, None, cs, gs[i][c], bs[i][c], st, None, o, 64, ws)
+
+    def two(i, c):
+        gb.gdn_conv_step(d, xs[i][c], w, None, cs, y, None, True)
+        gb.gdn_prefill_chunked(d, y, gs[i][c], bs[i][c], st, None, o, 64, ws)
+
+    res = {}
+    for name, fn in (("fused", fused), ("conv_step_then_prefill", two)):
+        for i in range(2):
+            for c in range(calls):
+                fn(i, c)
+        torch.cuda.synchronize()
+        graph = graph_of(torch, lambda: [fn(i, c) for i in range(nb) for c in range(calls)])
+        res[name + "_call_ms"] = time_graph(torch, graph, 3) / (nb * calls)
+        del graph
+    res["tokens_per_s_fused"] = sh.T / (res["fused_call_ms"] / 1e3)
+    res["saved_fraction"] = 1.0 - res["fused_call_ms"] / res["conv_step_then_prefill_call_ms"]
+    del xs, gs, bs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_gated_norm(torch, gb, W, args, ceil):
     """The gated RMSNorm after a 1,024-token prefill call (B1, 32 value / 16
     qk heads, d = 128, bf16 in and out): the call alone against the call
@@ -1025,6 +1073,7 @@ SECTIONS = {"per_layer": per_layer_cycle, "grouped": grouped_cycle, "lazy": lazy
             "solo": solo, "rewind": rewind, "conv_step": conv_step, "prefill": prefill,
             "prefill_ragged": prefill_ragged, "gated_rmsnorm": gated_rmsnorm,
             "verify_gated_norm": verify_gated_norm, "prefill_gated_norm": prefill_gated_norm,
+            "conv_prefill": conv_prefill,
             "ceilings": ceilings}
 
 EXTRA = (("grouped_verify_commit_b8_t2_l30", "grouped"), ("lazy_commit_verify_b8_t2", "lazy"),
@@ -1033,7 +1082,8 @@ EXTRA = (("grouped_verify_commit_b8_t2_l30", "grouped"), ("lazy_commit_verify_b8
          ("prefill_ragged_b8_up_to_1024", "prefill_ragged"),
          ("gated_rmsnorm_b8_t2_l30", "gated_rmsnorm"),
          ("verify_gated_norm_b8_t2_l30", "verify_gated_norm"),
-         ("prefill_gated_norm_b1_t1024", "prefill_gated_norm"))
+         ("prefill_gated_norm_b1_t1024", "prefill_gated_norm"),
+         ("conv_prefill_b1_4096_in_1024_calls", "conv_prefill"))
 
 CPU_LEGS = {"solo_b1_t3_l30": cpu_solo, "rewind_b8_t4_l30": cpu_rewind,
             "prefill_b1_4096_in_1024_calls": cpu_prefill}

@@ -87,6 +87,7 @@ _lib.gdn_prefill_ragged.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
 _lib.gdn_prefill_chunked.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
                                      ctypes.c_size_t, _vp, _vp]
 _lib.gdn_prefill_chunked_noalloc.argtypes = [_D, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp]
+_lib.gdn_prefill_conv_chunked.argtypes = [_D] + [_vp] * 9 + [_i32, _vp, ctypes.c_size_t, _vp, _vp]
 _lib.gdn_workspace_size.argtypes = [_D, _i32]
 _lib.gdn_workspace_size.restype = ctypes.c_size_t
 _lib.gdn_status_string.argtypes = [ctypes.c_int]
@@ -98,14 +99,14 @@ _lib.gdn_last_hip_error.restype = ctypes.c_char_p
 for _n in ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
            "gdn_accept_greedy", "gdn_gated_rmsnorm", "gdn_verify_gated_norm",
            "gdn_verify_lazy_gated_norm", "gdn_prefill_chunked", "gdn_prefill_ragged",
-           "gdn_prefill_chunked_noalloc"):
+           "gdn_prefill_chunked_noalloc", "gdn_prefill_conv_chunked"):
     getattr(_lib, _n).restype = ctypes.c_int
 
 EXPORTED = ("gdn_conv_step", "gdn_verify", "gdn_commit", "gdn_rewind", "gdn_verify_lazy",
             "gdn_accept_greedy", "gdn_gated_rmsnorm", "gdn_verify_gated_norm",
             "gdn_verify_lazy_gated_norm", "gdn_prefill_chunked", "gdn_prefill_ragged",
-            "gdn_prefill_chunked_noalloc", "gdn_workspace_size", "gdn_status_string", "gdn_version",
-            "gdn_last_hip_error")
+            "gdn_prefill_chunked_noalloc", "gdn_prefill_conv_chunked", "gdn_workspace_size",
+            "gdn_status_string", "gdn_version", "gdn_last_hip_error")
 
 
 def _torch():
@@ -326,6 +327,21 @@ def gdn_prefill_chunked(d, y, g, beta, state, cur, o, chunk=64, workspace=None, 
         _arg(cur, "cur", s["cur"], torch.int32, True), _arg(o, "o", s["o"], O), int(chunk),
         ws_ptr, ws_bytes, _arg(err, "err", s["err"], torch.int32, True), _stream(stream)),
         "gdn_prefill_chunked")
+
+
+def gdn_prefill_conv_chunked(d, x, conv_w, conv_b, conv_state, g, beta, state, cur, o, chunk=64,
+                             workspace=None, err=None, stream=None):
+    torch, s = _torch(), _shapes(d)
+    A, O = _act_dtype(d.act), _act_dtype(d.out)
+    ws_ptr, ws_bytes = _workspace(d, chunk, workspace)
+    _check(_lib.gdn_prefill_conv_chunked(
+        ctypes.byref(d), _arg(x, "x", s["x"], A), _arg(conv_w, "conv_w", s["conv_w"], A),
+        _arg(conv_b, "conv_b", s["conv_b"], A, True),
+        _arg(conv_state, "conv_state", s["conv_state"], A), _arg(g, "g", s["g"], A),
+        _arg(beta, "beta", s["g"], A), _arg(state, "state", s["state"], torch.float32),
+        _arg(cur, "cur", s["cur"], torch.int32, True), _arg(o, "o", s["o"], O), int(chunk),
+        ws_ptr, ws_bytes, _arg(err, "err", s["err"], torch.int32, True), _stream(stream)),
+        "gdn_prefill_conv_chunked")
 
 
 GDN_NOALLOC_SCRATCH_BYTES = 64 << 20

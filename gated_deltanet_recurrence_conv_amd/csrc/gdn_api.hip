@@ -202,15 +202,29 @@ gdn_status verify_lazy_impl(const gdn_dims* d, const void* x_prev, const void* g
 // Chunked prefill (padded or ragged).  With use_scratch the chunk records go
 // to the library's static device scratch instead of a caller's workspace;
 // dims whose records do not fit it are refused before anything is launched.
+// The fused conv's inputs (prefill_impl with conv = nullptr reads y).
+struct ConvIn {
+    const void* x;
+    const void* conv_w;
+    const void* conv_b;
+    void* conv_state;
+};
+
 gdn_status prefill_impl(const gdn_dims* d, const void* y, const void* g, const void* beta, float* state,
                         const int32_t* cur, void* o, const int32_t* lengths, int32_t chunk, void* workspace,
-                        size_t workspace_bytes, bool use_scratch, int32_t* err, void* stream)
+                        size_t workspace_bytes, bool use_scratch, int32_t* err, void* stream,
+                        const ConvIn* conv = nullptr)
 {
     gdn_status st = check_dims(d);
     if (st != GDN_OK) return st;
     if (chunk != 64) return GDN_E_SHAPE;
     st = check_ptrs({y, g, beta, state, o}, {workspace}, {cur, lengths, err});
     if (st != GDN_OK) return st;
+    if (conv) {
+        st = check_ptrs({conv->x, conv->conv_w, conv->conv_state}, {conv->conv_b}, {});
+        if (st != GDN_OK) return st;
+        if (!gdn::prefill_conv_supported(d->DK, d->DV, d->act)) return GDN_E_UNSUPPORTED;
+    }
     if (!gdn::prefill_supported(d->DK, d->DV, d->act)) return GDN_E_UNSUPPORTED;
     const size_t need = gdn::prefill_workspace_bytes(d->L, d->B, d->T, d->HV, d->DK, d->DV, d->act, chunk);
     if (use_scratch) {
@@ -226,6 +240,9 @@ gdn_status prefill_impl(const gdn_dims* d, const void* y, const void* g, const v
     p.L = d->L; p.B = d->B; p.T = d->T; p.HV = d->HV; p.HK = d->HK; p.S = d->S;
     p.C = channels(d); p.act = d->act; p.out = d->out;
     p.scale = d->scale; p.l2_eps = d->l2_eps; p.flags = d->flags;
+    if (conv) {
+        p.x = conv->x; p.conv_w = conv->conv_w; p.conv_b = conv->conv_b; p.conv_state = conv->conv_state;
+    }
     return from_hip(gdn::launch_prefill(p, d->DK, d->DV, static_cast<hipStream_t>(stream)));
 }
 
@@ -416,6 +433,17 @@ gdn_status gdn_prefill_chunked_noalloc(const gdn_dims* d, const void* y, const v
                                        void* stream)
 {
     return prefill_impl(d, y, g, beta, state, cur, o, nullptr, chunk, nullptr, 0, true, err, stream);
+}
+
+gdn_status gdn_prefill_conv_chunked(const gdn_dims* d, const void* x, const void* conv_w, const void* conv_b,
+                                    void* conv_state, const void* g, const void* beta, float* state,
+                                    const int32_t* cur, void* o, int32_t chunk, void* workspace,
+                                    size_t workspace_bytes, int32_t* err, void* stream)
+{
+    const ConvIn conv{x, conv_w, conv_b, conv_state};
+    // y is never read: x stands in for it in the pointer checks
+    return prefill_impl(d, x, g, beta, state, cur, o, nullptr, chunk, workspace, workspace_bytes, false, err,
+                        stream, &conv);
 }
 
 

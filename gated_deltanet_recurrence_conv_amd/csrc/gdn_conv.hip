@@ -17,26 +17,7 @@
 
 namespace gdn {
 
-// Loads/stores VEC contiguous activation values as fp32.
-template <int ACT>
-__device__ __forceinline__ void load_vec8(const void* base, size_t idx, float* v)
-{
-    if constexpr (ACT == ACT_BF16) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    } else {
-        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
-        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    }
-}
-
+// Stores 8 fp32 values as contiguous activation values (dt: the dtype).
 __device__ __forceinline__ void store_vec8(void* base, size_t idx, int dt, const float* v)
 {
     if (dt == ACT_BF16) {
@@ -126,23 +107,6 @@ hipError_t launch_window(const WinParams& p, hipStream_t s)
 // thread's loads are all in flight at once instead of one per token.
 constexpr int CONV_CT = 128;
 
-template <int ACT>
-__device__ __forceinline__ void to_f32x8(const uint4 (&raw)[ACT == ACT_BF16 ? 1 : 2], float* v)
-{
-    if constexpr (ACT == ACT_BF16) {
-        const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-        }
-    } else {
-        const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
-    }
-}
-
 template <int ACT, int TR>
 __global__ __launch_bounds__(CONV_CT) void conv_kernel(ConvParams p)
 {
@@ -169,23 +133,7 @@ __global__ __launch_bounds__(CONV_CT) void conv_kernel(ConvParams p)
         for (int v = 0; v < NV; ++v) raw[r][v] = reinterpret_cast<const uint4*>(src)[v];
     }
     float w[4][8], bias[8];
-    {
-        // conv_w[l][c][0..3] for 8 channels = 32 contiguous values.
-        float wr[32];
-        const size_t wi = (static_cast<size_t>(l) * p.C + c0) * 4;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) load_vec8<ACT>(p.conv_w, wi + 8 * q, wr + 8 * q);
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w[j][c] = wr[c * 4 + j];
-    }
-    if (p.conv_b) {
-        load_vec8<ACT>(p.conv_b, static_cast<size_t>(l) * p.C + c0, bias);
-    } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) bias[c] = 0.0f;
-    }
+    conv_taps8<ACT>(p.conv_w, p.conv_b, static_cast<size_t>(l) * p.C + c0, w, bias);
 
     const bool use_silu = (p.flags & FLAG_SILU) != 0;
     float win[4][8];
@@ -196,15 +144,7 @@ __global__ __launch_bounds__(CONV_CT) void conv_kernel(ConvParams p)
         const int t = t0 + i;
         to_f32x8<ACT>(raw[i + 3], win[3]);
         float yv[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            float acc = w[0][c] * win[0][c];
-            acc = fmaf(w[1][c], win[1][c], acc);
-            acc = fmaf(w[2][c], win[2][c], acc);
-            acc = fmaf(w[3][c], win[3][c], acc);
-            acc += bias[c];
-            yv[c] = use_silu ? silu_hw(acc) : acc;
-        }
+        conv8_token(w, win, bias, use_silu, yv);
         if (t < p.T) store_vec8(p.y, (static_cast<size_t>(lb) * p.T + t) * p.C + c0, p.out, yv);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {

@@ -127,6 +127,13 @@ struct PrefillParams {
     int32_t act, out;
     float scale, l2_eps;
     uint32_t flags;
+    // fused conv (x non-null): y is the short conv (+ SiLU) of [conv_state ; x],
+    // computed inside the prep kernel and rounded to the act dtype, and the
+    // scan kernel commits conv_state <- the last 3 window rows
+    const void* x;
+    const void* conv_w;
+    const void* conv_b;
+    void* conv_state;
 };
 // Greedy acceptance of a verification window.
 struct AcceptParams {
@@ -153,6 +160,7 @@ struct NormParams {
 hipError_t launch_gated_rmsnorm(const NormParams& p, hipStream_t s);
 
 bool prefill_supported(int DK, int DV, int act);
+bool prefill_conv_supported(int DK, int DV, int act);
 size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int act, int chunk);
 hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s);
 // fp32 form of the chunked prefill (fp32 activations, d_k = 16): no workspace.
@@ -219,6 +227,85 @@ __device__ __forceinline__ float silu_hw(float v)
 {
     return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
 }
+
+// Loads 8 contiguous activation values as fp32.
+template <int ACT>
+__device__ __forceinline__ void load_vec8(const void* base, size_t idx, float* v)
+{
+    if constexpr (ACT == ACT_BF16) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+}
+
+// 8 activation values held as raw 16-byte vectors -> fp32.
+template <int ACT>
+__device__ __forceinline__ void to_f32x8(const uint4 (&raw)[ACT == ACT_BF16 ? 1 : 2], float* v)
+{
+    if constexpr (ACT == ACT_BF16) {
+        const uint32_t w[4] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    } else {
+        const uint32_t w[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+    }
+}
+
+// Conv taps and bias of 8 consecutive channels (first channel index c0 of
+// layer l's [C] axis, i.e. l * C + channel): w[j][c] multiplies window row j
+// (row 3 = the token itself); a missing bias is 0.
+template <int ACT>
+__device__ __forceinline__ void conv_taps8(const void* conv_w, const void* conv_b, size_t lc0, float (&w)[4][8],
+                                           float (&bias)[8])
+{
+    // conv_w[l][c][0..3] for 8 channels = 32 contiguous values
+    float wr[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_vec8<ACT>(conv_w, lc0 * 4 + 8 * q, wr + 8 * q);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j][c] = wr[c * 4 + j];
+    if (conv_b) {
+        load_vec8<ACT>(conv_b, lc0, bias);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) bias[c] = 0.0f;
+    }
+}
+
+// The short causal conv (+ SiLU) of 8 channels at one token from its 4 window
+// rows; every kernel that computes the conv goes through this, so they all
+// produce the same bits.
+__device__ __forceinline__ void conv8_token(const float (&w)[4][8], const float (&win)[4][8], const float (&bias)[8],
+                                            bool use_silu, float (&y)[8])
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        float acc = w[0][c] * win[0][c];
+        acc = fmaf(w[1][c], win[1][c], acc);
+        acc = fmaf(w[2][c], win[2][c], acc);
+        acc = fmaf(w[3][c], win[3][c], acc);
+        acc += bias[c];
+        y[c] = use_silu ? silu_hw(acc) : acc;
+    }
+}
+
 
 // v + v[lane ^ OFF] across a wave64, OFF a power of two.  Lanes 8 apart
 // inside a 16-lane row trade values with a DPP row rotation (row_ror:8 maps

@@ -124,7 +124,7 @@ __device__ __forceinline__ uint4 frag_from_c(const f32x4& lo, const f32x4& hi)
 // prep kernel: one workgroup per (chunk, value head, layer*row).  Wave w owns
 // token tile w (tokens 16w..16w+15 of the chunk): the columns of its K K^T
 // and K Q^T products and the rows of P, U~ and W~.
-template <int DK, int DV>
+template <int DK, int DV, bool CONV>
 __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
 {
     using R = Rec<DK, DV>;
@@ -179,7 +179,80 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
     constexpr int NKV = DK / 32;                     // 16-byte K vectors per thread
     constexpr int NVV = (DV / 8 + 3) / 4;            // 16-byte V vectors per thread
     uint4 kv[NKV], vv[NVV], qf[KS];
-    {
+    if constexpr (CONV) {
+        // ---- y is the short conv (+ SiLU) of the window [conv_state ; x],
+        // rounded to bf16 as the conv step writes it (conv8_token: the same
+        // arithmetic).  K and V rows go straight to LDS: thread -> one group
+        // of 8 channels x TRC consecutive tokens, its TRC + 3 window rows
+        // loaded once.  Rows past the chunk are clamped onto its last token
+        // and their results are zero. ----
+        constexpr int GK = DK / 8, G = GK + DV / 8;
+        constexpr int NB = NTHR / G, TRC = (CH + NB - 1) / NB;
+        const bool silu = (p.flags & FLAG_SILU) != 0;
+        const uint16_t* xs = static_cast<const uint16_t*>(p.x);
+        const uint16_t* cst = static_cast<const uint16_t*>(p.conv_state);
+        const size_t lc = static_cast<size_t>(lb / p.B) * C;   // layer's first conv channel
+        // window row q of this (layer, row): conv cache row q (q < 3) or x row q - 3
+        auto wrow = [&](int q, size_t ch) -> uint4 {
+            return q < 3 ? *reinterpret_cast<const uint4*>(cst + (static_cast<size_t>(lb) * 3 + q) * C + ch)
+                         : *reinterpret_cast<const uint4*>(xs + (static_cast<size_t>(lb) * p.T + (q - 3)) * C + ch);
+        };
+        auto pack8 = [](const float (&v)[8]) {
+            return make_uint4(f32_to_bf16_bits(v[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16),
+                              f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16),
+                              f32_to_bf16_bits(v[4]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[5])) << 16),
+                              f32_to_bf16_bits(v[6]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[7])) << 16));
+        };
+        const int g = tid % G, j0 = (tid / G) * TRC;
+        if (tid < NB * G) {
+            const size_t ch = g < GK ? static_cast<size_t>(p.HK + m) * DK + 8 * g
+                                     : static_cast<size_t>(2 * p.HK) * DK + static_cast<size_t>(hv) * DV + 8 * (g - GK);
+            uint4 raw[TRC + 3];
+#pragma unroll
+            for (int r = 0; r < TRC + 3; ++r) raw[r] = wrow(t0 + min(j0 + r, n + 2), ch);
+            float wt4[4][8], bias[8], win[4][8];
+            conv_taps8<ACT_BF16>(p.conv_w, p.conv_b, lc + ch, wt4, bias);
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                const uint4 rr[1] = {raw[r]};
+                to_f32x8<ACT_BF16>(rr, win[r]);
+            }
+#pragma unroll
+            for (int k = 0; k < TRC; ++k) {
+                const int i = j0 + k;
+                const uint4 rr[1] = {raw[k + 3]};
+                to_f32x8<ACT_BF16>(rr, win[3]);
+                float yv[8];
+                conv8_token(wt4, win, bias, silu, yv);
+                const uint4 yb = i < n ? pack8(yv) : make_uint4(0, 0, 0, 0);
+                if (i < CH) {
+                    if (g < GK) *reinterpret_cast<uint4*>(&Ks[i][8 * g]) = yb;
+                    else *reinterpret_cast<uint4*>(&Vs[i][8 * (g - GK)]) = yb;
+                }
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    win[0][c] = win[1][c];
+                    win[1][c] = win[2][c];
+                    win[2][c] = win[3][c];
+                }
+            }
+        }
+        // Q fragments of token 16 w + fr, each from its own 4 window rows
+        const int tq = min(16 * w + fr, n - 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const size_t ch = static_cast<size_t>(m) * DK + 32 * ks + fk;
+            float wt4[4][8], bias[8], win[4][8], yv[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint4 rr[1] = {wrow(t0 + tq + j, ch)};
+                to_f32x8<ACT_BF16>(rr, win[j]);
+            }
+            conv_taps8<ACT_BF16>(p.conv_w, p.conv_b, lc + ch, wt4, bias);
+            conv8_token(wt4, win, bias, silu, yv);
+            qf[ks] = pack8(yv);
+        }
+    } else {
         const size_t row = (ybase + min(lr, n - 1)) * C;
 #pragma unroll
         for (int q = 0; q < NKV; ++q)
@@ -199,10 +272,15 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
     // ---- rows into LDS, norms, gates ----
     const bool lreal = lr < n;
     float sk = 0.f;
+    if constexpr (CONV) {
+        lds_barrier();   // the conv wrote the K and V rows; read this thread's K vectors back
+#pragma unroll
+        for (int q = 0; q < NKV; ++q) kv[q] = *reinterpret_cast<const uint4*>(&Ks[lr][8 * (sub + 4 * q)]);
+    }
 #pragma unroll
     for (int q = 0; q < NKV; ++q) {
         if (!lreal) kv[q] = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(&Ks[lr][8 * (sub + 4 * q)]) = kv[q];
+        if constexpr (!CONV) *reinterpret_cast<uint4*>(&Ks[lr][8 * (sub + 4 * q)]) = kv[q];
         const uint32_t kw[4] = {kv[q].x, kv[q].y, kv[q].z, kv[q].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -213,8 +291,10 @@ __global__ __launch_bounds__(NTHR, 2) void prefill_prep_kernel(PrefillParams p)
     }
 #pragma unroll
     for (int q = 0; q < NVV; ++q) {
-        if (!lreal) vv[q] = make_uint4(0, 0, 0, 0);
-        if (sub + 4 * q < DV / 8) *reinterpret_cast<uint4*>(&Vs[lr][8 * (sub + 4 * q)]) = vv[q];
+        if constexpr (!CONV) {
+            if (!lreal) vv[q] = make_uint4(0, 0, 0, 0);
+            if (sub + 4 * q < DV / 8) *reinterpret_cast<uint4*>(&Vs[lr][8 * (sub + 4 * q)]) = vv[q];
+        }
     }
     sk += __shfl_xor(sk, 1, 64);   // the 4 threads of a token row are consecutive lanes
     sk += __shfl_xor(sk, 2, 64);
@@ -687,6 +767,45 @@ __device__ __forceinline__ void out_wave(const PrefillParams& p, Ring<DK> (&ring
     }
 }
 
+// Fused conv: the conv cache of row lb becomes window rows T .. T+2 of
+// [conv_state ; x], as the conv step commits it.  The prep kernel, which read
+// the old cache, has finished before this kernel starts.  This workgroup's
+// share: the v channels of its column slices of value head hv and, in the
+// workgroups of the qk head's first value head, a strided part of the q and k
+// channels of qk head m; thread i of the two output waves takes every 128th
+// channel of that share, reading its three source rows before writing them
+// (for T < 3 some sources are cache rows further down).
+template <int DK, int DV, int SL>
+__device__ __forceinline__ void conv_commit(const PrefillParams& p, int lb, int m, int hv, int gsz, int cs, int i)
+{
+    constexpr int NSW = DV / 16 / SL;    // workgroups per value head
+    constexpr int NQK = (2 * DK + NSW - 1) / NSW;   // q/k channels per workgroup (at most)
+    const size_t C = p.C;
+    uint16_t* cst = static_cast<uint16_t*>(p.conv_state);
+    const uint16_t* xs = static_cast<const uint16_t*>(p.x);
+    const bool first = hv == m * gsz;
+    const int nv = 16 * SL, nt = nv + (first ? NQK : 0);
+    for (int e = i; e < nt; e += 128) {
+        size_t ch;
+        if (e < nv) {
+            ch = 2 * static_cast<size_t>(p.HK) * DK + static_cast<size_t>(hv) * DV + 16 * SL * cs + e;
+        } else {
+            const int k = cs + NSW * (e - nv);   // q (k < DK) or k (DK <= k < 2 DK) channel of head m
+            if (k >= 2 * DK) continue;
+            ch = k < DK ? static_cast<size_t>(m) * DK + k : static_cast<size_t>(p.HK) * DK + m * DK + (k - DK);
+        }
+        uint16_t v[3];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const int q = p.T + r;   // window row that becomes cache row r
+            v[r] = q < 3 ? cst[(static_cast<size_t>(lb) * 3 + q) * C + ch]
+                         : xs[(static_cast<size_t>(lb) * p.T + (q - 3)) * C + ch];
+        }
+#pragma unroll
+        for (int r = 0; r < 3; ++r) cst[(static_cast<size_t>(lb) * 3 + r) * C + ch] = v[r];
+    }
+}
+
 template <int DK, int DV, int OUT, int SL>
 __global__ __launch_bounds__(64 * (SL + 2)) void prefill_scan_kernel(PrefillParams p)
 {
@@ -770,10 +889,10 @@ __global__ __launch_bounds__(64 * (SL + 2)) void prefill_scan_kernel(PrefillPara
         for (int a = 0; a < DK / 16; ++a)
 #pragma unroll
             for (int j = 0; j < 4; ++j) st[(16 * a + fq + j) * DV + col] = h[a][j];
-    } else if (w == SL) {
-        out_wave<DK, DV, OUT, 0, 3, SL>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
     } else {
-        out_wave<DK, DV, OUT, 1, 2, SL>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
+        if (p.x) conv_commit<DK, DV, SL>(p, lb, m, hv, gsz, cs, (w - SL) * 64 + lane);
+        if (w == SL) out_wave<DK, DV, OUT, 0, 3, SL>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
+        else out_wave<DK, DV, OUT, 1, 2, SL>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
     }
 }
 
@@ -784,8 +903,12 @@ hipError_t launch_pf(const PrefillParams& p, hipStream_t s)
     const long long rows = static_cast<long long>(p.L) * p.B;
     if (NC > 0x7fffffff || p.HV > 65535 || rows > 65535) return hipErrorInvalidConfiguration;
     clear_stale_error();
-    hipLaunchKernelGGL((prefill_prep_kernel<DK, DV>), dim3(NC, p.HV, static_cast<unsigned>(rows)),
-                       dim3(NTHR), 0, s, p);
+    if (p.x)
+        hipLaunchKernelGGL((prefill_prep_kernel<DK, DV, true>), dim3(NC, p.HV, static_cast<unsigned>(rows)),
+                           dim3(NTHR), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_prep_kernel<DK, DV, false>), dim3(NC, p.HV, static_cast<unsigned>(rows)),
+                           dim3(NTHR), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // One 16-column slice per workgroup while there are no more one-slice
@@ -853,6 +976,12 @@ bool prefill_supported(int DK, int DV, int act)
            (DV == 16 || DV == 32 || DV == 64 || DV == 128);
 }
 
+// The fused conv runs inside the bf16 prep kernel only.
+bool prefill_conv_supported(int DK, int DV, int act)
+{
+    return prefill_supported(DK, DV, act) && bf16_path(DK, act);
+}
+
 size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int act, int chunk)
 {
     if (chunk != CH) return 0;
@@ -870,7 +999,7 @@ size_t prefill_workspace_bytes(int L, int B, int T, int HV, int DK, int DV, int 
 
 hipError_t launch_prefill(const PrefillParams& p, int DK, int DV, hipStream_t s)
 {
-    if (!bf16_path(DK, p.act)) return launch_prefill_f32(p, DK, DV, s);
+    if (!bf16_path(DK, p.act)) return p.x ? hipErrorInvalidValue : launch_prefill_f32(p, DK, DV, s);
     switch (DK) {
     case 32: return launch_pf_dv<32>(p, DV, s);
     case 64: return launch_pf_dv<64>(p, DV, s);

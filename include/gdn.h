@@ -263,6 +263,26 @@ gdn_status gdn_prefill_ragged(const gdn_dims* d, const void* y, const void* g, c
                               int32_t chunk, void* workspace, size_t workspace_bytes,
                               int32_t* err, void* stream);
 
+/* Prompt prefill from the raw projection ([P2] Functional commits items 2
+ * and 4: the short conv with its cache mutated in place; [P1] Measurements:
+ * prompts prefilled in 1,024-token calls): equals gdn_conv_step(d with
+ * out = act, x, conv_w, conv_b, conv_state, y, active = NULL,
+ * commit_state = 1) followed by gdn_prefill_chunked(d, y, g, beta, state,
+ * cur, o, chunk, workspace) bit for bit, without writing y: the conv (+ SiLU
+ * when GDN_FLAG_CONV_SILU is set) is computed inside the prefill and rounded to
+ * the act dtype as the conv step would store it, and conv_state ends as the
+ * last KCONV-1 window rows of [conv_state ; x].  bf16 activations with
+ * DK >= 32 only; other shapes return GDN_E_UNSUPPORTED (use the two calls).
+ * x: [L][B][T][C] act dtype; conv_w, conv_b, conv_state as for
+ * gdn_conv_step; workspace as for gdn_prefill_chunked.  A row whose slot is
+ * out of range gets GDN_ERR_SLOT and is left untouched, conv_state included
+ * (the two-call sequence would have committed its conv cache). */
+gdn_status gdn_prefill_conv_chunked(const gdn_dims* d, const void* x, const void* conv_w,
+                                    const void* conv_b, void* conv_state, const void* g,
+                                    const void* beta, float* state, const int32_t* cur, void* o,
+                                    int32_t chunk, void* workspace, size_t workspace_bytes,
+                                    int32_t* err, void* stream);
+
 /* gdn_prefill_chunked without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): the chunk records go to a static device

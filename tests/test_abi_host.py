@@ -74,6 +74,30 @@ def verify_call(lib, d, **over):
              args["beta"], args["st"], args["cur"], args["o"], args["act"], args["err"], None)
 
 
+def declared_param_counts():
+    """Number of parameters of every function include/gdn.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"^\s*(?:gdn_status|size_t|const char\*)\s+(gdn_\w+)\s*\(([^)]*)\)", text, re.M):
+        args = m.group(2).strip()
+        out[m.group(1)] = 0 if args in ("", "void") else args.count(",") + 1
+    return out
+
+
+def test_binding_declares_every_argument():
+    """Each C function the binding calls has ctypes argtypes with the header's
+    parameter count, so no 64-bit pointer is ever passed as a C int."""
+    from gated_deltanet_recurrence_conv_amd import binding
+    src = open(binding.__file__).read()
+    called = set(re.findall(r"_lib\.(gdn_\w+)\(", src))
+    counts = declared_param_counts()
+    assert called <= set(counts)
+    for n in called:
+        argtypes = getattr(binding._lib, n).argtypes
+        assert argtypes is not None, n
+        assert len(argtypes) == counts[n], (n, len(argtypes), counts[n])
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("act", 7, 3), ("out", -1, 3), ("L", 0, 2), ("B", 0, 2), ("T", 0, 2), ("T", 5, 2),
     ("HV", 30, 2), ("DK", 96, 2), ("DV", 8, 2), ("KCONV", 3, 2), ("S", 2, 2)])
@@ -127,6 +151,28 @@ def test_commit_rewind_conv_prefill_validation(lib):
     lib.gdn_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32]
     lib.gdn_workspace_size.restype = ctypes.c_size_t
     assert lib.gdn_workspace_size(ctypes.byref(d), 32) == 0
+
+
+def test_prefill_conv_validation(lib):
+    """The fused conv + prefill: missing pointers, chunk, workspace size, and
+    the shapes it does not serve (fp32 activations, d_k = 16)."""
+    f = lib.gdn_prefill_conv_chunked
+    f.argtypes = [ctypes.POINTER(Dims)] + [ctypes.c_void_p] * 9 + \
+        [ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+
+    def call(d, conv_w=FAKE, chunk=64, ws_bytes=1 << 40):
+        return f(ctypes.byref(d), FAKE, conv_w, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, chunk,
+                 FAKE, ws_bytes, None, None)
+    d = good()
+    d.T = 1024
+    assert call(d, conv_w=None) == 1
+    assert call(d, chunk=32) == 2
+    assert call(d, ws_bytes=16) == 6
+    d.act = 0                     # fp32 activations: the two calls serve them
+    assert call(d) == 5
+    d = good()
+    d.DK = 16
+    assert call(d) == 5
 
 
 def test_verify_lazy_validation(lib):
