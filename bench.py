@@ -578,9 +578,10 @@ def lazy_legs(torch, gb, W, args, ceil):
     verifies the new window without candidate writes.  Per layer (30 calls
     per cycle, as a model forward issues them) and grouped (one call over the
     30 layers); same pools, keep sequence and graph replay as the headline.
-    Each call is two launches (the replay-and-verify kernel and the
-    conv-cache shift); the roofline prices the whole cycle's bytes against
-    its time."""
+    A one-layer call is one launch (its workgroups, one per qk head, also
+    shift the conv cache); the 30-layer call is two (the replay-and-verify
+    kernel and the conv-cache shift).  The roofline prices the whole cycle's
+    bytes against its time."""
     sh = W.COHORT
     big, t, rng, act_rows = cohort_pools(torch, W, sh, L_POOL, 1001)
     d1 = gb.make_dims(1, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16", out="f32")
@@ -607,7 +608,7 @@ def lazy_legs(torch, gb, W, args, ceil):
 
     res = {}
     byts = float(np.mean([lazy_bytes(sh, keeps[i - 1], act_rows, L_POOL) for i in range(args.warmup, n)]))
-    for name, cyc, launches, tkey in (("per_layer", cycle_layers, 2 * L_POOL, None),
+    for name, cyc, launches, tkey in (("per_layer", cycle_layers, L_POOL, None),
                                       ("grouped", cycle_grouped, 2, "lazy_b8_t2_l30")):
         for i in range(args.warmup):
             cyc(i)

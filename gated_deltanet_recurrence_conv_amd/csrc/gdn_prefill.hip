@@ -806,7 +806,7 @@ __device__ __forceinline__ void conv_commit(const PrefillParams& p, int lb, int 
     }
 }
 
-template <int DK, int DV, int OUT, int SL>
+template <int DK, int DV, int OUT, int SL, bool CONV>
 __global__ __launch_bounds__(64 * (SL + 2)) void prefill_scan_kernel(PrefillParams p)
 {
     using R = Rec<DK, DV>;
@@ -890,10 +890,28 @@ __global__ __launch_bounds__(64 * (SL + 2)) void prefill_scan_kernel(PrefillPara
 #pragma unroll
             for (int j = 0; j < 4; ++j) st[(16 * a + fq + j) * DV + col] = h[a][j];
     } else {
-        if (p.x) conv_commit<DK, DV, SL>(p, lb, m, hv, gsz, cs, (w - SL) * 64 + lane);
+        if constexpr (CONV) conv_commit<DK, DV, SL>(p, lb, m, hv, gsz, cs, (w - SL) * 64 + lane);
         if (w == SL) out_wave<DK, DV, OUT, 0, 3, SL>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
         else out_wave<DK, DV, OUT, 1, 2, SL>(p, ring, recs, recs_kq, NCr, len, lb, hv, cs, lane);
     }
+}
+
+// The scan instantiations: output dtype x slices per workgroup x fused conv
+// (whose cache commit is compiled only where it is used).
+template <int DK, int DV, bool CONV>
+void launch_scan(const PrefillParams& p, dim3 grid, bool two, hipStream_t s)
+{
+    if constexpr (DV >= 32) {
+        if (two) {
+            if (p.out == ACT_BF16)
+                hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16, 2, CONV>), grid, dim3(256), 0, s, p);
+            else
+                hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32, 2, CONV>), grid, dim3(256), 0, s, p);
+            return;
+        }
+    }
+    if (p.out == ACT_BF16) hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16, 1, CONV>), grid, dim3(192), 0, s, p);
+    else hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32, 1, CONV>), grid, dim3(192), 0, s, p);
 }
 
 template <int DK, int DV>
@@ -924,19 +942,8 @@ hipError_t launch_pf(const PrefillParams& p, hipStream_t s)
     const long long blocks = two ? blocks1 / 2 : blocks1;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks));
-    if constexpr (DV >= 32) {
-        if (two) {
-            if (p.out == ACT_BF16)
-                hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16, 2>), grid, dim3(256), 0, s, p);
-            else
-                hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32, 2>), grid, dim3(256), 0, s, p);
-            return hipGetLastError();
-        }
-    }
-    {
-        if (p.out == ACT_BF16) hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_BF16, 1>), grid, dim3(192), 0, s, p);
-        else hipLaunchKernelGGL((prefill_scan_kernel<DK, DV, ACT_F32, 1>), grid, dim3(192), 0, s, p);
-    }
+    if (p.x) launch_scan<DK, DV, true>(p, grid, two, s);
+    else launch_scan<DK, DV, false>(p, grid, two, s);
     return hipGetLastError();
 }
 
