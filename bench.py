@@ -608,7 +608,7 @@ def lazy_legs(torch, gb, W, args, ceil):
 
     res = {}
     byts = float(np.mean([lazy_bytes(sh, keeps[i - 1], act_rows, L_POOL) for i in range(args.warmup, n)]))
-    for name, cyc, launches, tkey in (("per_layer", cycle_layers, L_POOL, None),
+    for name, cyc, launches, tkey in (("per_layer", cycle_layers, L_POOL, "lazy_per_layer_b8_t2_l30"),
                                       ("grouped", cycle_grouped, 2, "lazy_b8_t2_l30")):
         for i in range(args.warmup):
             cyc(i)
