@@ -929,16 +929,20 @@ hipError_t launch_pf(const PrefillParams& p, hipStream_t s)
                            dim3(NTHR), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // One 16-column slice per workgroup while there are no more one-slice
-    // workgroups than compute units (the slice's chain sets the time);
-    // larger grids put two slices of a head in each workgroup, whose output
-    // waves serve both.  The test is against the CU count, not against
-    // residency: a one-slice workgroup uses 412 VGPRs per lane in its state
-    // wave, so a CU holds one of them at a time.
+    // One 16-column slice per workgroup, or two slices of a head per
+    // workgroup whose output waves serve both.  A scan workgroup uses 412
+    // VGPRs per lane in its state wave, so a CU holds one at a time and a grid
+    // runs in rounds of CU-count workgroups.  A two-slice round costs about
+    // 1.4-1.75 one-slice rounds (1,024-token calls at 32 heads, d = 128: B = 2
+    // 63.8 against 67.8 us, B = 3 101-103 against 96.4 us, B = 4 120 against
+    // 129 us, B = 8 257-262 against 305 us, two against one slice), so two
+    // slices are taken when 5 r2 < 3 r1 for r1, r2 the rounds of the two grids.
     const long long groups = rows * p.HK;
     const long long blocks1 = (groups + 7) / 8 * 8 * (p.HV / p.HK) * (DV / 16);
     const int cus = device_cus();
-    const bool two = DV >= 32 && cus > 0 && blocks1 > cus;
+    const long long r1 = cus > 0 ? (blocks1 + cus - 1) / cus : 0;
+    const long long r2 = cus > 0 ? (blocks1 / 2 + cus - 1) / cus : 0;
+    const bool two = DV >= 32 && cus > 0 && 5 * r2 < 3 * r1;
     const long long blocks = two ? blocks1 / 2 : blocks1;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(blocks));

@@ -308,15 +308,18 @@ def test_prefill_ragged_bad_length_reported():
 
 
 def scan_slices_per_workgroup(rows, HV, HK, DV):
-    """The scan form the library launches: two 16-column slices per workgroup
-    when the one-slice grid (rows x qk heads padded to a multiple of 8, x
-    value heads per qk head x DV/16 slices) exceeds the GPU's compute units
-    and DV >= 32, else one."""
+    """The scan form the library launches: with the one-slice grid (rows x qk
+    heads padded to a multiple of 8, x value heads per qk head x DV/16
+    slices) taking r1 rounds of one workgroup per compute unit and the
+    two-slice grid r2, two 16-column slices per workgroup when DV >= 32 and
+    5 r2 < 3 r1, else one."""
     torch = torch_mod()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     groups = rows * HK
     blocks1 = (groups + 7) // 8 * 8 * (HV // HK) * (DV // 16)
-    return 2 if DV >= 32 and blocks1 > cus else 1
+    r1 = -(-blocks1 // cus)
+    r2 = -(-(blocks1 // 2) // cus)
+    return 2 if DV >= 32 and 5 * r2 < 3 * r1 else 1
 
 
 @pytest.mark.parametrize("DK,DV,lengths,out", [
