@@ -210,21 +210,38 @@ def algorithmic_min_bytes(sh, keep, active, L):
 
 
 def lazy_bytes(sh, keep_prev, act_rows, L):
-    """Algorithmic bytes of one fused commit + verify cycle over L layers:
-    per (layer, row) that replays or verifies, one state read, both windows'
-    x (2T rows) and the conv cache (3 rows), both windows' g and beta; per
-    committing row one state write and the conv-cache shift (3 rows read, 3
-    written); per active row the outputs; per layer the conv weights."""
+    """Algorithmic bytes of one fused commit + verify cycle over L layers: per
+    (layer, row) that replays or verifies, one state read and the 3 conv-cache
+    rows; per replayed token its x row and g, beta (keep_prev tokens of the
+    previous window); per active row the new window's x, g, beta and its fp32
+    outputs; per committing row one state write and the 3 new conv-cache rows;
+    per layer the conv weights.  (The kernels also read the previous window's
+    unreplayed rows and, on 30-layer grids, re-read the new cache rows in the
+    shift launch: counted traffic, not algorithmic bytes.)"""
     esz = 2 if sh.act == "bf16" else 4
     tile = sh.HV * sh.DK * sh.DV * 4
+    tok = sh.C * esz + 2 * sh.HV * esz          # one token's x row, g and beta
     per = 0
     for b in range(sh.B):
-        if act_rows[b] or keep_prev[b] > 0:
-            per += tile + (2 * sh.T + 3) * sh.C * esz + 4 * sh.T * sh.HV * esz
-        if keep_prev[b] > 0:
-            per += tile + 6 * sh.C * esz
+        kp = int(keep_prev[b])
+        if act_rows[b] or kp > 0:
+            per += tile + 3 * sh.C * esz + kp * tok
+        if kp > 0:
+            per += tile + 3 * sh.C * esz
         if act_rows[b]:
-            per += sh.T * sh.HV * sh.DV * 4
+            per += sh.T * tok + sh.T * sh.HV * sh.DV * 4
+    return L * (per + sh.C * 4 * esz)
+
+
+def rewind_bytes(sh, keep, L):
+    """Algorithmic bytes of one rewind over L layers: per committing (layer,
+    row) the state tile read and written back, the keep replayed tokens' x
+    rows and g, beta, the 3 conv-cache rows read and the 3 new ones written;
+    per layer the conv weights.  (On 30-layer grids the shift launch re-reads
+    the new cache rows: counted traffic, not algorithmic bytes.)"""
+    esz = 2 if sh.act == "bf16" else 4
+    tile = sh.HV * sh.DK * sh.DV * 4
+    per = sum(2 * tile + int(kk) * (sh.C * esz + 2 * sh.HV * esz) + 6 * sh.C * esz for kk in keep if kk > 0)
     return L * (per + sh.C * 4 * esz)
 
 
@@ -706,12 +723,7 @@ def rewind(torch, gb, W, args, ceil):
     torch.cuda.synchronize()
     graph = graph_of(torch, lambda: [call(i) for i in range(3, reps + 3)])
     ms = time_graph(torch, graph, 1, warm=1) / reps
-    tile = sh.HV * sh.DK * sh.DV * 4
-    k = keeps_np[3:]
-    # per committing (layer, row): state read + written, keep tokens of x/g/beta,
-    # conv cache read + written (3 rows each) and the conv weights' share
-    per_call = np.mean([L_POOL * sum(2 * tile + kk * (sh.C * 2 + 4 * sh.HV) + 9 * sh.C * 2
-                                     for kk in row if kk > 0) for row in k])
+    per_call = np.mean([rewind_bytes(sh, row, L_POOL) for row in keeps_np[3:]])
     assert int(t["err"].item()) == 0
     del t, graph
     torch.cuda.empty_cache()
