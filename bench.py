@@ -594,8 +594,10 @@ def lazy_legs(torch, gb, W, args, ceil):
     tokens from the snapshot, writes the committed state once in place, and
     verifies the new window without candidate writes.  Per layer (30 calls
     per cycle, as a model forward issues them) and grouped (one call over the
-    30 layers); same pools, keep sequence and graph replay as the headline.
-    A one-layer call is one launch (its workgroups, one per qk head, also
+    30 layers); the headline's pools, 3 untimed and 20 timed cycles of seeded
+    keeps, replayed from a graph.  The sample is fixed (not --steps) so that
+    the bytes priced here and the counters of a profiled run come from the
+    same keep vectors.  A one-layer call is one launch (its workgroups, one per qk head, also
     shift the conv cache); the 30-layer call is two (the replay-and-verify
     kernel and the conv-cache shift).  The roofline prices the whole cycle's
     bytes against its time."""
@@ -604,7 +606,8 @@ def lazy_legs(torch, gb, W, args, ceil):
     d1 = gb.make_dims(1, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16", out="f32")
     dL = gb.make_dims(L_POOL, sh.B, sh.T, sh.HV, sh.HK, sh.DK, sh.DV, S=sh.S, act="bf16",
                       out="f32")
-    n = args.steps + args.warmup
+    warm, cycles = 3, 20
+    n = warm + cycles
     keeps = np.stack([W.keep_uniform(rng, sh, act_rows) for _ in range(n)]).astype(np.int32)
     keep_d = torch.from_numpy(keeps).cuda()
 
@@ -624,15 +627,15 @@ def lazy_legs(torch, gb, W, args, ceil):
         call(dL, slice(0, L_POOL), i)
 
     res = {}
-    byts = float(np.mean([lazy_bytes(sh, keeps[i - 1], act_rows, L_POOL) for i in range(args.warmup, n)]))
+    byts = float(np.mean([lazy_bytes(sh, keeps[i - 1], act_rows, L_POOL) for i in range(warm, n)]))
     for name, cyc, launches, tkey in (("per_layer", cycle_layers, L_POOL, "lazy_per_layer_b8_t2_l30"),
                                       ("grouped", cycle_grouped, 2, "lazy_b8_t2_l30")):
-        for i in range(args.warmup):
+        for i in range(warm):
             cyc(i)
         torch.cuda.synchronize()
 
         def timed():
-            for i in range(args.warmup, n):
+            for i in range(warm, n):
                 cyc(i)
         graph = graph_of(torch, timed)
         tm = Timer(torch)
@@ -640,7 +643,7 @@ def lazy_legs(torch, gb, W, args, ceil):
         graph.replay()
         end = tm.ev()
         torch.cuda.synchronize()
-        ms = start.elapsed_time(end) / args.steps
+        ms = start.elapsed_time(end) / cycles
         assert int(t["err"].item()) == 0, "device error word set"
         del graph
         gbs = byts / (ms / 1e3) / 1e9
