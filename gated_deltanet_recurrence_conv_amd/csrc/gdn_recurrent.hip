@@ -112,9 +112,16 @@ constexpr int waves_per_wg()
     return GRP ? kGroupMaxWaves : (NORM ? waves_per_head<DV>() : 1) * ksplit<DK, DV>();
 }
 
-template <int DK, int DV, int ACT, bool LAZY, bool NORM, bool GRP>
+// LZ: 0 for verify and rewind; for the fused form (LAZY) the most tokens a
+// wave runs, a replayed prefix of at most T tokens plus a window of T: 4 when
+// T <= 2, 8 when T <= 4.  The conv outputs in LDS and the window and gate
+// registers are sized by it, and the T <= 2 instantiation's halved LDS lets
+// more waves share a CU (30-layer B8/T2 cohort: fused cycle 152-156 against
+// 141-144 us; one-layer launches 456 against 440 us per 30-layer cycle).
+template <int DK, int DV, int ACT, int LZ, bool NORM, bool GRP>
 __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM, GRP>())) void recurrent_kernel(RecParams p)
 {
+    constexpr bool LAZY = LZ > 0;
     constexpr int SW = DV < 32 ? DV : 32;  // columns per wave
     constexpr int NS = DV / SW;            // column slices per head
     constexpr int JL = SW / 4;             // lanes across one row segment
@@ -122,7 +129,7 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM, GRP>())) void recu
     constexpr int KS = ksplit<DK, DV>();   // d_k parts (waves) per slice
     constexpr int KR = DK / KS;            // rows of one part
     constexpr int RPL = KR / IG;           // rows held per lane
-    constexpr int MAXT = LAZY ? 8 : 4;     // tokens one wave runs
+    constexpr int MAXT = LAZY ? LZ : 4;    // tokens one wave runs
     constexpr int NW = NORM ? NS : 1;      // column slices per workgroup (NORM)
     constexpr int NWG = NW * KS;           // waves per workgroup (not GRP)
     // conv channels of the workgroup: q and k of the qk head, then the v
@@ -575,14 +582,14 @@ static size_t occupancy_lds_bytes(size_t static_bytes, int wg_per_cu)
 // Static LDS of one kernel instantiation, queried once per process (the
 // cache is a static of this function template, so each instantiation has its
 // own).
-template <int DK, int DV, int ACT, bool LAZY, bool NORM, bool GRP>
+template <int DK, int DV, int ACT, int LZ, bool NORM, bool GRP>
 static size_t static_lds()
 {
     static std::atomic<long long> cached{-1};
     long long v = cached.load(std::memory_order_relaxed);
     if (v < 0) {
         hipFuncAttributes a{};
-        if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(recurrent_kernel<DK, DV, ACT, LAZY, NORM, GRP>)) !=
+        if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(recurrent_kernel<DK, DV, ACT, LZ, NORM, GRP>)) !=
             hipSuccess) {
             clear_stale_error();
             return 0;   // no cap can be derived; the launch then runs uncapped
@@ -593,19 +600,28 @@ static size_t static_lds()
     return static_cast<size_t>(v);
 }
 
-template <int DK, int DV, int ACT, bool LAZY, bool NORM, bool GRP>
+template <int DK, int DV, int ACT, int LZ, bool NORM, bool GRP>
 static void launch_one(const RecParams& p, dim3 grid, int threads, int cap, hipStream_t s)
 {
-    const size_t st = cap > 0 ? static_lds<DK, DV, ACT, LAZY, NORM, GRP>() : 0;
+    const size_t st = cap > 0 ? static_lds<DK, DV, ACT, LZ, NORM, GRP>() : 0;
     const size_t dyn = cap > 0 && st > 0 ? occupancy_lds_bytes(st, cap) : 0;
-    hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT, LAZY, NORM, GRP>), grid, dim3(threads), dyn, s, p);
+    hipLaunchKernelGGL((recurrent_kernel<DK, DV, ACT, LZ, NORM, GRP>), grid, dim3(threads), dyn, s, p);
 }
 
-template <int DK, int DV, bool LAZY, bool NORM, bool GRP = false>
+template <int DK, int DV, int LZ, bool NORM, bool GRP = false>
 static void launch_rec_act(const RecParams& p, dim3 grid, int threads, int cap, hipStream_t s)
 {
-    if (p.act == ACT_BF16) launch_one<DK, DV, ACT_BF16, LAZY, NORM, GRP>(p, grid, threads, cap, s);
-    else launch_one<DK, DV, ACT_F32, LAZY, NORM, GRP>(p, grid, threads, cap, s);
+    if (p.act == ACT_BF16) launch_one<DK, DV, ACT_BF16, LZ, NORM, GRP>(p, grid, threads, cap, s);
+    else launch_one<DK, DV, ACT_F32, LZ, NORM, GRP>(p, grid, threads, cap, s);
+}
+
+// The fused form's instantiation by its token capacity (T <= 4 is checked
+// by the caller).
+template <int DK, int DV, bool NORM, bool GRP = false>
+static void launch_lazy_act(const RecParams& p, dim3 grid, int threads, int cap, hipStream_t s)
+{
+    if (p.T <= 2) launch_rec_act<DK, DV, 4, NORM, GRP>(p, grid, threads, cap, s);
+    else launch_rec_act<DK, DV, 8, NORM, GRP>(p, grid, threads, cap, s);
 }
 
 template <int DK, int DV>
@@ -638,8 +654,8 @@ static hipError_t launch_rec(RecParams p, hipStream_t s, bool* conv_shifted)
         const int waves = lazy ? kLazyWavesPerCU : kRewindWavesPerCU;
         const int cap = waves > 0 ? (waves / wpw > 0 ? waves / wpw : 1) : 0;
         clear_stale_error();
-        if (lazy) launch_rec_act<DK, DV, true, false, true>(p, dim3(static_cast<unsigned>(blocks)), 64 * wpw, cap, s);
-        else launch_rec_act<DK, DV, false, false, true>(p, dim3(static_cast<unsigned>(blocks)), 64 * wpw, cap, s);
+        if (lazy) launch_lazy_act<DK, DV, false, true>(p, dim3(static_cast<unsigned>(blocks)), 64 * wpw, cap, s);
+        else launch_rec_act<DK, DV, 0, false, true>(p, dim3(static_cast<unsigned>(blocks)), 64 * wpw, cap, s);
         return hipGetLastError();
     }
     p.conv_out = nullptr;
@@ -659,11 +675,11 @@ static hipError_t launch_rec(RecParams p, hipStream_t s, bool* conv_shifted)
     const dim3 grid(static_cast<unsigned>(blocks));
     clear_stale_error();
     if (lazy) {
-        if (norm) launch_rec_act<DK, DV, true, true>(p, grid, 64 * wpw, cap, s);
-        else launch_rec_act<DK, DV, true, false>(p, grid, 64 * wpw, cap, s);
+        if (norm) launch_lazy_act<DK, DV, true>(p, grid, 64 * wpw, cap, s);
+        else launch_lazy_act<DK, DV, false>(p, grid, 64 * wpw, cap, s);
     } else {
-        if (norm) launch_rec_act<DK, DV, false, true>(p, grid, 64 * wpw, cap, s);
-        else launch_rec_act<DK, DV, false, false>(p, grid, 64 * wpw, cap, s);
+        if (norm) launch_rec_act<DK, DV, 0, true>(p, grid, 64 * wpw, cap, s);
+        else launch_rec_act<DK, DV, 0, false>(p, grid, 64 * wpw, cap, s);
     }
     return hipGetLastError();
 }
