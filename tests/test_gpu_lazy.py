@@ -64,8 +64,9 @@ def lazy(r, bd, keep):
 
 # Head shapes beyond the cohort's, fp32 (1e-5): value heads per qk head times
 # column slices per head sets how many waves a qk head's workgroup holds; the
-# last shape has more than one workgroup holds, so its conv cache is shifted by
-# a second launch.
+# g4 shapes have more than one workgroup holds, so their conv cache is shifted
+# by a second launch.  The kernel is built for windows of T <= 2 and of
+# T <= 4 separately; both sizes run in both layouts (T = 1 and 2, T = 3 and 4).
 DIM_SHAPES = {
     "cohort": W.COHORT,
     "rewind": W.REWIND,
@@ -74,6 +75,9 @@ DIM_SHAPES = {
     "k16_v128": W.Shape("k16_v128", L=2, B=3, T=4, HV=4, HK=2, DK=16, DV=128, S=5, act="f32"),
     "g1_v64": W.Shape("g1_v64", L=2, B=3, T=2, HV=4, HK=4, DK=32, DV=64, S=4, act="f32", inactive=(2,)),
     "g4_v128": W.Shape("g4_v128", L=2, B=3, T=3, HV=8, HK=2, DK=64, DV=128, S=4, act="f32"),
+    "t1_k32": W.Shape("t1_k32", L=2, B=3, T=1, HV=4, HK=2, DK=32, DV=32, S=2, act="f32", inactive=(1,)),
+    "t4_g4": W.Shape("t4_g4", L=2, B=3, T=4, HV=8, HK=2, DK=32, DV=128, S=5, act="f32", inactive=(2,)),
+    "t1_g4": W.Shape("t1_g4", L=1, B=4, T=1, HV=8, HK=2, DK=64, DV=128, S=3, act="f32"),
 }
 
 
