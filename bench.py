@@ -762,7 +762,7 @@ def conv_step(torch, gb, W, args, ceil):
     gbs = byts / (ms / 1e3) / 1e9
     return dict(tokens=sh.T, ms_per_call=ms, bytes_per_call=byts, gbs=gbs,
                 roofline=roofline("hbm", gbs, HBM_PEAK_GBS, "GB/s", "conv_kernel_t1024_c8192",
-                                  measured_peak=ceil.get("copy_gbs"), kernel="gdn::conv_kernel<bf16,8>",
+                                  measured_peak=ceil.get("copy_gbs"), kernel="gdn::conv_kernel<bf16,4>",
                                   algorithmic_bytes_per_launch=byts, avg_launch_ms=ms))
 
 
