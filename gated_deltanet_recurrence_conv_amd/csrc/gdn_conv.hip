@@ -17,7 +17,14 @@
 
 namespace gdn {
 
-// Stores 8 fp32 values as contiguous activation values (dt: the dtype).
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Stores 8 fp32 values as contiguous activation values (dt: the dtype),
+// non-temporally: a 1,024-token call's 16.8 MB of y is written in one burst at
+// the end of its waves, and streaming it out instead of leaving it dirty in
+// the L2 until the kernel ends took the call from 10.7 to 8.6 us (32 heads,
+// d = 128, C = 8,192).  The prefill that reads y next then finds it in HBM
+// rather than in the MALL; the conv step + prefill pair measured the same.
 __device__ __forceinline__ void store_vec8(void* base, size_t idx, int dt, const float* v)
 {
     if (dt == ACT_BF16) {
@@ -26,11 +33,12 @@ __device__ __forceinline__ void store_vec8(void* base, size_t idx, int dt, const
         raw.y = f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
         raw.z = f32_to_bf16_bits(v[4]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[5])) << 16);
         raw.w = f32_to_bf16_bits(v[6]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[7])) << 16);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) = raw;
+        __builtin_nontemporal_store(__builtin_bit_cast(v4u, raw), reinterpret_cast<v4u*>(static_cast<uint16_t*>(base) + idx));
     } else {
-        float4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
-        *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = a;
-        *reinterpret_cast<float4*>(static_cast<float*>(base) + idx + 4) = b;
+        const v4u a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        const v4u b = {__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])};
+        __builtin_nontemporal_store(a, reinterpret_cast<v4u*>(static_cast<float*>(base) + idx));
+        __builtin_nontemporal_store(b, reinterpret_cast<v4u*>(static_cast<float*>(base) + idx + 4));
     }
 }
 
@@ -81,11 +89,13 @@ __global__ __launch_bounds__(WIN_THREADS) void window_kernel(WinParams p)
             buf[r][0] = reinterpret_cast<const uint4*>(src)[0];
             if (esz == 4) buf[r][1] = reinterpret_cast<const uint4*>(src)[1];
         }
+        // non-temporal: the grouped commit over 30 layers x 8 rows ran ~2.5 us
+        // shorter than with plain stores (the next launch reads the cache from HBM)
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
             char* dst = static_cast<char*>(p.conv_state) + ((static_cast<size_t>(lb) * 3 + r) * p.C + c0) * esz;
-            reinterpret_cast<uint4*>(dst)[0] = buf[r][0];
-            if (esz == 4) reinterpret_cast<uint4*>(dst)[1] = buf[r][1];
+            __builtin_nontemporal_store(__builtin_bit_cast(v4u, buf[r][0]), reinterpret_cast<v4u*>(dst));
+            if (esz == 4) __builtin_nontemporal_store(__builtin_bit_cast(v4u, buf[r][1]), reinterpret_cast<v4u*>(dst) + 1);
         }
     }
 }
