@@ -35,6 +35,10 @@ __device__ __forceinline__ void load8(const void* base, size_t idx, float* v)
     }
 }
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// y is streamed out non-temporally (cohort over 30 layers: 5.47 -> 5.33 us per
+// call against plain stores).
 template <int DT>
 __device__ __forceinline__ void store8(void* base, size_t idx, const float* v)
 {
@@ -44,11 +48,12 @@ __device__ __forceinline__ void store8(void* base, size_t idx, const float* v)
         raw.y = f32x2_to_bf16x2(v[2], v[3]);
         raw.z = f32x2_to_bf16x2(v[4], v[5]);
         raw.w = f32x2_to_bf16x2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) = raw;
+        __builtin_nontemporal_store(__builtin_bit_cast(v4u, raw), reinterpret_cast<v4u*>(static_cast<uint16_t*>(base) + idx));
     } else {
-        const float4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
-        *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = a;
-        *reinterpret_cast<float4*>(static_cast<float*>(base) + idx + 4) = b;
+        const v4u a = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        const v4u b = {__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])};
+        __builtin_nontemporal_store(a, reinterpret_cast<v4u*>(static_cast<float*>(base) + idx));
+        __builtin_nontemporal_store(b, reinterpret_cast<v4u*>(static_cast<float*>(base) + idx + 4));
     }
 }
 

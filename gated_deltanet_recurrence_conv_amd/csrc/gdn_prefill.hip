@@ -577,16 +577,18 @@ template <int DK, int DV>
 __device__ __forceinline__ void k_load(KFrags<DK, DV>& f, rsrc_t r, rsrc_t rk, int lane16, int vq16, int cs)
 {
     using R = Rec<DK, DV>;
+    // in the order the chunk uses them (the compiler starts the chunk with
+    // the decay's multiply of H, and loads complete in order): the decay, U~,
+    // the scalings, then K^T (1,024-token call: 37.6 -> 36.6 us on one box)
+    f.gC = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 0, R::VEC + 2 * CH * 4, 0));
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        f.ut[tb] = bload16(r, lane16, R::UT + (tb * (DV / 16) + cs) * 1024);
-        f.ks[tb] = bload16(r, vq16, R::VEC + (CH + 16 * tb) * 4);
-    }
+    for (int tb = 0; tb < 4; ++tb) f.ut[tb] = bload16(r, lane16, R::UT + (tb * (DV / 16) + cs) * 1024);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) f.ks[tb] = bload16(r, vq16, R::VEC + (CH + 16 * tb) * 4);
 #pragma unroll
     for (int a = 0; a < DK / 16; ++a)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) f.kt[a][ks] = bload16(rk, lane16, R::KT + (a * 2 + ks) * 1024);
-    f.gC = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, 0, R::VEC + 2 * CH * 4, 0));
 }
 
 template <int DK>
