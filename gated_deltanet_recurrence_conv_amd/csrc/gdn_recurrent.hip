@@ -358,13 +358,16 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM, GRP>())) void recu
     const bool l2 = (p.flags & FLAG_L2) != 0;
     for (int t = 0; t < nsteps; ++t) {
         const int tout = LAZY ? t - kp : t;   // token of the window o belongs to
-        // A rewind without o needs neither h^T q nor |q| and k.q (a uniform
-        // branch; u and h are computed the same way in both).  The fused form
-        // keeps one step body for its replayed and verified tokens: with two
-        // (the replayed ones reduced like the rewind's) its 30-layer cohort
-        // cycle measured 171 against 148-152 us.
+        // A step without an output (a rewind without o, a replayed token of
+        // the fused form) needs neither h^T q nor |q| and k.q (a uniform
+        // branch; u and h are computed the same way in both, so the fused form
+        // stays bit-equal to rewind + verify).  With the 4-token window the
+        // fused form's replayed steps take the short body (B8/T2 cohort: one
+        // layer per launch 419 -> 395 us per 30-layer cycle, 30 layers in one
+        // launch 140-146 -> 138-139 us); with the 8-token window the two bodies
+        // measured slower (171 against 148-152 us), so every step there is full.
         const bool want_out = p.o != nullptr && tout >= 0;
-        const bool full_step = LAZY || want_out;
+        const bool full_step = want_out || LZ == 8;
         float kr[RPL], qr[RPL];
 #pragma unroll
         for (int r = 0; r < RPL; ++r) kr[r] = ys[t][DK + row0 + ig + IG * r];
