@@ -304,9 +304,10 @@ __global__ __launch_bounds__((64 * waves_per_wg<DK, DV, NORM, GRP>())) void recu
         h[r] = __builtin_nontemporal_load(reinterpret_cast<const f4*>(src + (row0 + ig + IG * r) * DV));
 
     // ---- conv + SiLU for every window token, into LDS (a rewind without o
-    // needs no q channels) ----
+    // needs no q channels, nor do the replayed tokens of the 4-token fused
+    // form, whose steps skip the q work) ----
     const bool use_silu = (p.flags & FLAG_SILU) != 0;
-    const int qskip = LAZY ? 0 : (p.mode == REC_REWIND && !p.o ? nsteps : 0);
+    const int qskip = LAZY ? (LZ == 4 ? kp : 0) : (p.mode == REC_REWIND && !p.o ? nsteps : 0);
 #pragma unroll
     for (int n = 0; n < NG; ++n) {
         const int ch = lane + 64 * (wid + nwg * n);
