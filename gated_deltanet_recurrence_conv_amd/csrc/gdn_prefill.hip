@@ -120,6 +120,8 @@ __device__ __forceinline__ uint4 frag_from_c(const f32x4& lo, const f32x4& hi)
     return cvt8(v);
 }
 
+// Raw buffer resources: the prep kernel's record stores and every load and
+// store of the scan kernel go through them.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int RSRC_WORD3 = 0x00020000;   // raw (stride 0) buffer, 32-bit data format
 
